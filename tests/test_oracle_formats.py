@@ -1,0 +1,247 @@
+"""Pins of the oracle's number formats and page layouts against closed forms,
+library routines (torch's e8m0 and e4m3 dtypes) and brute force.
+
+Sources: OCP Microscaling Formats (MX) v1.0 for e2m1 / e8m0 and the scale
+rule; ATOM PR #2812 ("Mono decode over the MXFP4 KV and index caches") for the
+8704-byte page and the saturating e4m3 q store.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+from oracle import formats as F
+import workloads as W
+
+
+# ---------------------------------------------------------------- page sizes
+def test_page_sizes_closed_form():
+    # 128 tokens x 128 elements x 4 bits + one e8m0 byte per 32 elements
+    assert F.MXFP4_PAGE_BYTES == 128 * 128 // 2 + 128 * 128 // 32 == 8704
+    # 128 x 128 e4m3 bytes + one fp32 scale per token
+    assert F.FP8_PAGE_BYTES == 128 * 128 + 128 * 4 == 16896
+
+
+# ---------------------------------------------------------------- e2m1
+def test_e2m1_table_is_ocp_fp4():
+    # OCP MX v1.0, FP4 E2M1: the 8 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert list(F.E2M1_TABLE[:8]) == mags
+    assert list(F.E2M1_TABLE[8:]) == [-m for m in mags]
+    assert math.copysign(1.0, F.E2M1_TABLE[8]) == -1.0
+
+
+def test_e2m1_roundtrip_all_codes():
+    vals = F.E2M1_TABLE.copy()
+    vals[8] = -0.0
+    assert list(F.e2m1_encode(vals)) == list(range(16))
+
+
+def test_e2m1_midpoints_round_half_even():
+    # every midpoint between neighbouring magnitudes goes to the code with mantissa bit 0
+    mid = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    want = [0, 2, 2, 4, 4, 6, 6]            # 0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0
+    assert list(F.e2m1_encode(np.array(mid))) == want
+    assert list(F.e2m1_encode(-np.array(mid))) == [c | 8 for c in want]
+
+
+def test_e2m1_saturation_and_sign():
+    assert list(F.e2m1_encode(np.array([6.0, 6.5, 7.99, 1e30]))) == [7, 7, 7, 7]
+    assert list(F.e2m1_encode(np.array([-7.0, -1e-30, -0.0]))) == [15, 8, 8]
+
+
+def test_e2m1_nearest_brute_force():
+    rng = np.random.default_rng(11)
+    v = np.concatenate([rng.uniform(-7, 7, 4000), rng.standard_normal(1000) * 0.3])
+    codes = F.e2m1_encode(v)
+    for x, c in zip(v, codes):
+        a = min(abs(x), 6.0)
+        best = min(range(8), key=lambda k: (abs(a - F.E2M1_TABLE[k]), k & 1))
+        assert (c & 7) == best and (c >> 3) == (1 if x < 0 or (x == 0 and math.copysign(1, x) < 0) else 0)
+
+
+# ---------------------------------------------------------------- e8m0
+def test_e8m0_matches_torch_all_bytes():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
+    got = F.e8m0_value(np.arange(256))
+    assert np.isnan(ref[255]) and np.isnan(got[255])
+    np.testing.assert_array_equal(got[:255], ref[:255])
+
+
+def test_scale_byte_brackets_amax():
+    rng = np.random.default_rng(3)
+    amax = np.ldexp(rng.uniform(1, 2, 5000), rng.integers(-120, 120, 5000))
+    b = F.mx_scale_byte(amax)
+    # OCP: 2^(b - 127) is the largest power of two with amax / 2^(b-127) < 8,
+    # i.e. 2^(b-127+2) <= amax < 2^(b-127+3)
+    assert np.all(np.ldexp(1.0, b - 127 + 2) <= amax)
+    assert np.all(amax < np.ldexp(1.0, b - 127 + 3))
+
+
+def test_scale_byte_worked_values():
+    assert F.mx_scale_byte(1.0) == 125           # 1 = 4 * 2^-2
+    assert F.mx_scale_byte(6.0) == 127
+    assert F.mx_scale_byte(7.9) == 127
+    assert F.mx_scale_byte(8.0) == 128
+    assert F.mx_scale_byte(0.0) == 0
+    assert F.mx_scale_byte(1e-45) == 0           # fp32 subnormal: clamps to 2^-127
+    assert F.mx_scale_byte(2.0 ** -125) == 0     # floor(log2) - 2 = -127 -> byte 0
+    assert F.mx_scale_byte(2.0 ** -124) == 1
+    for k in range(-100, 101, 7):
+        assert F.mx_scale_byte(6.0 * 2.0 ** k) == 127 + k
+
+
+# ---------------------------------------------------------------- MXFP4 rows
+def test_quantize_worked_rows():
+    x = np.zeros((1, 128), dtype=np.float32)
+    x[0, :32] = 1.0                      # amax 1 -> byte 125 -> 1.0 / 0.25 = 4.0 -> code 6
+    x[0, 32] = 6.0                       # amax 6 -> byte 127, 6 -> code 7, rest 0
+    x[0, 64] = 7.9                       # amax 7.9 -> byte 127, 7.9 clips to 6 -> code 7
+    x[0, 65] = -2.5                      # -2.5 at scale 1 -> tie -> -2.0 -> code 0xC
+    codes, sb = F.mxfp4_quantize_rows(x)
+    assert list(sb[0]) == [125, 127, 127, 0]
+    assert list(codes[0, :32]) == [6] * 32
+    assert codes[0, 32] == 7 and (codes[0, 33:64] == 0).all()
+    assert codes[0, 64] == 7 and codes[0, 65] == 0xC
+    assert (codes[0, 96:] == 0).all()    # all-zero group: byte 0, codes 0
+
+
+def test_quantize_roundtrip_on_grid():
+    """Rows already on an MX grid (each group holds a magnitude 4 or 6) survive
+    quantize(dequantize(.)) exactly, codes and scale bytes alike."""
+    rng = np.random.default_rng(5)
+    N = 512
+    codes = rng.integers(0, 16, size=(N, 128)).astype(np.uint8)
+    for g in range(4):                               # force the group's amax code
+        codes[:, 32 * g + rng.integers(0, 32)] = rng.choice([6, 7, 14, 15], size=N)
+    sb = rng.integers(2, 250, size=(N, 4)).astype(np.uint8)
+    x = F.mxfp4_dequantize(codes, sb).astype(np.float32)
+    c2, s2 = F.mxfp4_quantize_rows(x)
+    np.testing.assert_array_equal(s2, sb)
+    np.testing.assert_array_equal(c2, codes)
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(0, 2**31 - 1))
+def test_quantize_error_bound(seed):
+    x = np.random.default_rng(seed).standard_normal((4, 128)).astype(np.float32) * 3
+    codes, sb = F.mxfp4_quantize_rows(x)
+    dq = F.mxfp4_dequantize(codes, sb).reshape(4, 4, 32)
+    scale = np.ldexp(1.0, sb.astype(np.int64) - 127)[..., None]
+    err = np.abs(dq - x.reshape(4, 4, 32)) / scale
+    # gap between e2m1 neighbours is at most 2 (4 -> 6), values in (6, 8) clip: error < 2
+    assert err.max() < 2.0
+    # below 2 the grid step is 0.5: error at most 0.25 there
+    small = np.abs(x.reshape(4, 4, 32)) / scale < 2.0
+    assert (err[small] <= 0.25).all()
+
+
+# ---------------------------------------------------------------- e4m3
+def _torch_e4m3(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_in_range_matches_torch():
+    rng = np.random.default_rng(7)
+    vals = F.E4M3_TABLE[:127]
+    mids = (vals[:-1] + vals[1:]) / 2                      # every tie between neighbours
+    x = np.concatenate([
+        rng.standard_normal(20000) * 50, rng.standard_normal(5000) * 1e-2,
+        rng.uniform(-448, 448, 20000), mids, -mids, vals, -vals,
+        np.nextafter(mids.astype(np.float32), np.float32(0)),
+        np.nextafter(mids.astype(np.float32), np.float32(1e9)),
+    ]).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    np.testing.assert_array_equal(F.e4m3_encode(x), _torch_e4m3(x))
+
+
+def test_e4m3_saturates_and_keeps_nan():
+    x = np.array([448.0, 449.0, 464.0, 500.0, 1e30, np.inf, -500.0, -np.inf, np.nan, -np.nan, -0.0],
+                 dtype=np.float32)
+    got = F.e4m3_encode(x)
+    assert list(got[:6]) == [0x7E] * 6
+    assert list(got[6:8]) == [0xFE] * 2
+    assert got[8] in (0x7F, 0xFF) and got[9] in (0x7F, 0xFF)
+    assert got[10] == 0x80
+    assert np.isnan(F.E4M3_TABLE[0x7F]) and F.E4M3_TABLE[0x7E] == 448.0
+
+
+def test_e4m3_clamp_negative_control():
+    """Without the clamp the cast turns large values into NaN (torch does so
+    above 464), and the saturation check above catches it."""
+    x = np.array([500.0, np.inf], dtype=np.float32)
+    assert list(_torch_e4m3(x)) != list(F.e4m3_encode(x))
+
+
+# ---------------------------------------------------------------- FP8 rows (reading)
+def test_fp8_rows_roundtrip_bound():
+    x = np.random.default_rng(9).standard_normal((300, 128)).astype(np.float32)
+    x[0] = 0.0
+    codes, scale = F.fp8_quantize_rows(x)
+    assert scale[0] == 1.0 and (codes[0] == 0).all()
+    dq = F.E4M3_TABLE[codes.astype(np.int64)] * scale[:, None].astype(np.float64)
+    # e4m3 keeps 3 mantissa bits: relative error <= 2^-4 for normals, absolute
+    # <= 2^-10 * scale in the subnormal range
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scale[:, None])
+    assert (np.abs(dq - x) <= bound + 1e-30).all()
+    # the largest element lands on +-448
+    i = np.abs(x[1:]).argmax(axis=1)
+    assert set(np.unique(codes[1:][np.arange(299), i] & 0x7F)) == {0x7E}
+
+
+# ---------------------------------------------------------------- pages
+@pytest.mark.parametrize("fmt", ["mxfp4", "fp8"])
+def test_store_read_and_poison(fmt):
+    rng = np.random.default_rng(2)
+    L = 300                                            # 3 pages, last one partly filled
+    table = np.array([5, 1, 3], dtype=np.int32)
+    pool = W.new_pool(7, F.PAGE_BYTES[fmt])
+    x = rng.standard_normal((L, 128)).astype(np.float32)
+    F.STORE[fmt](pool, table, 0, x[:200])
+    F.STORE[fmt](pool, table, 200, x[200:])            # second write continues the sequence
+    got = F.READ[fmt](pool, table, L)
+    if fmt == "mxfp4":
+        want = F.mxfp4_dequantize(*F.mxfp4_quantize_rows(x))
+    else:
+        c, s = F.fp8_quantize_rows(x)
+        want = F.E4M3_TABLE[c.astype(np.int64)] * s[:, None].astype(np.float64)
+    np.testing.assert_array_equal(got, want)
+    pages = pool.reshape(7, -1)
+    for p in (0, 2, 4, 6):                             # pages never written stay poisoned
+        assert (pages[p] == 0xFF).all()
+    # the unwritten tail of page 3 (tokens 44..127) still reads as NaN
+    tail = F.READ[fmt](pool, np.array([5, 1, 3], dtype=np.int32), 384, np.arange(300, 384))
+    assert np.isnan(tail).all()
+
+
+def test_mxfp4_byte_layout():
+    """Token t of a page: 64 data bytes at 64 t (element 2i low nibble), 4 scale
+    bytes at 8192 + 4 t."""
+    x = np.zeros((2, 128), dtype=np.float32)
+    x[1, 0] = 0.5                 # group 0: amax 0.5 -> byte 124 (2^-3), 0.5 -> 4.0 -> code 6
+    x[1, 1] = -0.5                # code 0xE
+    x[1, 127] = 6.0               # group 3: byte 127, code 7 in the high nibble of byte 63
+    pool = W.new_pool(1, F.MXFP4_PAGE_BYTES)
+    F.mxfp4_store(pool, np.array([0], dtype=np.int32), 0, x)
+    row1 = pool[64:128]
+    assert row1[0] == 0xE6 and row1[63] == 0x70 and (row1[1:63] == 0).all()
+    assert list(pool[8192 + 4:8192 + 8]) == [124, 0, 0, 127]
+    assert list(pool[8192:8196]) == [0, 0, 0, 0]
+    assert (pool[128:8192] == 0xFF).all() and (pool[8200:] == 0xFF).all()
+
+
+def test_page_table_permutation_invariance():
+    """Relabelling physical pages (and moving their bytes) leaves every read bit-identical."""
+    rng = np.random.default_rng(4)
+    L = 1000
+    table = rng.permutation(12)[:8].astype(np.int32)
+    pool = W.new_pool(12, F.MXFP4_PAGE_BYTES)
+    F.mxfp4_store(pool, table, 0, rng.standard_normal((L, 128)).astype(np.float32))
+    perm = rng.permutation(12)
+    pool2 = np.empty_like(pool).reshape(12, -1)
+    pool2[perm] = pool.reshape(12, -1)
+    a = F.mxfp4_read(pool, table, L)
+    b = F.mxfp4_read(pool2.reshape(-1), perm[table].astype(np.int32), L)
+    np.testing.assert_array_equal(a, b)
