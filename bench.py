@@ -1,0 +1,229 @@
+"""Benchmark of the sparse-attention decode step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload headline]
+
+One step = the whole hot path of one decode step over one batch: row store of
+the step's new K / V / index rows, e4m3 query store, index scores over every
+page, top-k, split attention over the selected pages and the merge
+(decode_step of libmxsparse, replayed as a HIP graph). The default workload is
+the 256K-context one: B = 4 sequences x q = 8 query rows (1 + 7 drafts), 16
+query heads per KV head, head_dim 128, MXFP4 K / V / index caches, top-k 32.
+
+Inputs are resident in HBM before timing starts. Each timed step runs on the
+next of R cache replicas (R * ~90 MB touched per step > the 256 MB Infinity
+Cache), so the index scan streams from HBM, not from the MALL; the one-replica
+(warm) number is reported separately.
+
+Prints one JSON line (rank 0): the metric (query rows/s), the whole step's
+algorithmic HBM bytes and GB/s, the roofline of the dominant kernel (the index
+scorer: 100 back-to-back launches over rotating replicas captured in one HIP
+graph, timed with HIP events on the stream they run on) and the oracle's
+throughput on a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+PAGE_MX = 8704
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(inp, table: np.ndarray) -> dict:
+    """Bytes the step must move at minimum: every index page of every sequence
+    once, the distinct K and V pages the sequence's rows selected, the new rows
+    (read as fp32, stored as MXFP4), the query, index query, weights, page table
+    and the bf16 output with its lse."""
+    wl = inp.wl
+    idx_pages = int(sum((int(L) + 127) // 128 for L in inp.contexts))
+    kv_pages = 0
+    for b in range(wl.B):
+        kv_pages += len(np.unique(table[b][table[b] >= 0]))
+    rows = wl.B * wl.q
+    other = (3 * rows * 128 * 4 + 3 * rows * 68            # new rows in, stored rows out
+             + rows * wl.H * 128 * 4                      # fp32 query
+             + rows * wl.H_I * 128 * 2 + rows * wl.H_I * 4  # index query, weights
+             + wl.B * inp.max_pages * 4 + wl.B * 4        # page table, contexts
+             + rows * wl.H * 128 * 2 + rows * wl.H * 4)   # output bf16, lse
+    return {"index_pages": idx_pages * PAGE_MX, "kv_pages": 2 * kv_pages * PAGE_MX, "other": other,
+            "total": idx_pages * PAGE_MX + 2 * kv_pages * PAGE_MX + other,
+            "n_index_pages": idx_pages, "n_kv_pages": 2 * kv_pages}
+
+
+def cpu_baseline(inp, min_seconds=10.0, max_seconds=30.0) -> dict:
+    """The oracle (NumPy, float64) on sequence 0 of the workload: its whole
+    decode step (row store of the new rows, scores over every page, top-k,
+    attention), repeated until at least ``min_seconds`` of CPU work."""
+    from threadpoolctl import threadpool_info
+    from oracle import step as OS
+    wl = inp.wl
+    fmts = {"k": wl.kv_format, "v": wl.kv_format, "idx": wl.idx_format}
+    pools = {s: OS.build_cache(inp, s, f, seqs=[0]) for s, f in fmts.items()}
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        OS.decode_step_ref(inp, pools=pools, seqs=[0])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or el + el / reps > max_seconds:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": reps * wl.q / el, "unit": "query rows/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"sequence 0 of {wl.B} ({wl.q} query rows, {int(inp.contexts[0])}-token context): the "
+                      f"oracle's full step for that sequence, {reps} run(s) in {el:.1f} s; "
+                      f"host affinity {len(os.sched_getaffinity(0))} cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--replicas", type=int, default=6)
+    ap.add_argument("--scorer-launches", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the decode step of one rank is a "
+                                   "single-GPU kernel chain with no collectives; run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    import sparse_attention_decode_mxfp4_amd as mx
+    import workloads as W
+    import workloads.gpu as WG
+
+    torch.cuda.set_device(0)
+    mx.lib()
+    wl = W.WORKLOADS[args.workload]
+    inp = W.make_inputs(wl)
+    t_setup = time.perf_counter()
+    pools0 = WG.fill_prefix(inp, WG.empty_pools(inp))
+    torch.cuda.synchronize()
+    log(f"[bench] filled {wl.name} caches in {time.perf_counter() - t_setup:.1f} s")
+    t = WG.step_tensors(inp)
+    R = max(1, args.replicas)
+    replicas = [pools0] + [{s: p.clone() for s, p in pools0.items()} for _ in range(R - 1)]
+    caches = [WG.make_cache(inp, p) for p in replicas]
+    tables = [torch.empty((wl.B, wl.q, wl.topk), dtype=torch.int32, device="cuda") for _ in range(R)]
+    steps = [mx.DecodeStep(c, t["query"], t["q_idx"], t["w"], wl.topk, wl.sm_scale, k_new=t.get("k_new"),
+                           v_new=t.get("v_new"), idx_new=t.get("idx_new"), block_table_out=tb)
+             for c, tb in zip(caches, tables)]
+    for s in steps:
+        s.run()
+    torch.cuda.synchronize()
+    ab = algorithmic_bytes(inp, tables[0].cpu().numpy())
+
+    # ---- the timed region: K steps, rotating replicas
+    if args.eager:
+        runs = [s.run for s in steps]
+    else:
+        graphs = []
+        for s in steps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                s.run()
+            graphs.append(g)
+        runs = [g.replay for g in graphs]
+    for i in range(args.warmup):
+        runs[i % R]()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        runs[i % R]()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    ev_ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # warm (MALL-resident) number: one replica
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(args.steps):
+        runs[0]()
+    ev1.record()
+    torch.cuda.synchronize()
+    warm_ms = ev0.elapsed_time(ev1) / args.steps
+
+    # ---- the dominant kernel: the index scorer, K back-to-back launches (rotating
+    # replicas) captured in one HIP graph, timed with HIP events on the stream
+    # it runs on; the average includes the short gap between graph nodes
+    scores = [torch.empty((wl.B, wl.q, inp.max_pages), dtype=torch.float32, device="cuda") for _ in range(R)]
+    for i in range(R):
+        mx.index_score(caches[i], t["q_idx"], t["w"], scores[i])
+    torch.cuda.synchronize()
+    n_launch = args.scorer_launches
+    gs = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gs):
+        for i in range(n_launch):
+            mx.index_score(caches[i % R], t["q_idx"], t["w"], scores[i % R])
+    gs.replay()
+    torch.cuda.synchronize()
+    ev0.record()
+    gs.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    score_us = ev0.elapsed_time(ev1) * 1e3 / n_launch
+    score_bytes = ab["index_pages"] + ab["n_index_pages"] * wl.q * 4 + wl.B * wl.q * wl.H_I * (256 + 4)
+    score_gbps = score_bytes / (score_us * 1e-6) / 1e9
+
+    rows = wl.B * wl.q
+    step_gbps = ab["total"] / (ms_step * 1e-3) / 1e9
+    out = {
+        "metric": "decode sparse-attn query rows/s + HBM GB/s (% peak), 256K ctx, B=4, q=8",
+        "value": rows / (ms_step * 1e-3),
+        "unit": "query rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: B={wl.B}, q={wl.q} (1+{wl.q - 1} drafts), {wl.H}:1 GQA, head_dim 128, "
+                        f"context {int(inp.contexts.min())}..{int(inp.contexts.max())} tokens, "
+                        f"{wl.kv_format} K/V, {wl.idx_format} index, top-k {wl.topk}, {wl.H_I} index heads, "
+                        f"full decode_step ({'eager' if args.eager else 'HIP graph replay'})",
+            "B": wl.B, "q": wl.q, "H": wl.H, "H_I": wl.H_I, "topk": wl.topk,
+            "context": int(inp.contexts.max()), "cache_replicas": R,
+            "arithmetic": "bf16 MFMA for index scores, QK and PV (fp4 / e4m3 widened exactly to bf16), f32 accumulate",
+        },
+        "hbm": {"algorithmic_bytes_per_step": ab["total"], "GBps": step_gbps, "peak_GBps": HBM_PEAK_GBPS,
+                "frac": step_gbps / HBM_PEAK_GBPS, "index_bytes": ab["index_pages"],
+                "kv_bytes": ab["kv_pages"], "other_bytes": ab["other"]},
+        "event_ms_per_step": ev_ms_step,
+        "warm_mall_ms_per_step": warm_ms,
+        "roofline": {"bound": "hbm", "kernel": "index scorer (k_index_score)", "achieved": score_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": score_gbps / HBM_PEAK_GBPS,
+                     "traffic": None, "avg_launch_us": score_us, "algorithmic_bytes_per_launch": score_bytes},
+    }
+    log(f"[bench] step {ms_step * 1e3:.1f} us (events {ev_ms_step * 1e3:.1f} us, warm {warm_ms * 1e3:.1f} us), "
+        f"{step_gbps:.0f} GB/s; scorer {score_us:.1f} us = {score_gbps:.0f} GB/s")
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

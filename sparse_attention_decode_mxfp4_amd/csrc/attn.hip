@@ -1,0 +1,331 @@
+// Split-KV sparse attention over the selected pages.
+//
+// ATOM PR #2812, "Mono decode over the MXFP4 KV and index caches", commit
+// message of the MXFP4 main-KV commit: the split stage reads the K and V pages
+// of the sparse (block) table — one selected block is one 128-token page —
+// and writes per-partition partials sp_o / sp_m / sp_l for a merge. There, QK
+// is one MX-scaled 16x16x128 MFMA (K fp4 with its e8m0 group scale against
+// the e4m3 query) and PV a bf16 MFMA over V widened to bf16. This kernel keeps
+// the matrix-core split of work but lays the operands out its own way:
+//
+// * Workgroup = (partition p, query row j, sequence b), 4 waves. Partition p
+//   owns block-table slots [p c, min((p+1) c, topk)), c = ceil(topk / P); wave
+//   w takes every 4th of them, keeps an online softmax (m, l, O) for the 16
+//   heads, and the 4 waves merge through LDS into one partial.
+// * QK: D[token][head] = K[token][:] . q[head][:] on v_mfma_f32_16x16x32_bf16.
+//   Lane 16 kg + n loads token n's group kg — 16 bytes and one scale byte, the
+//   same coalesced pattern as the index scorer — and widens it to bf16 with
+//   the group scale (exact); the e4m3 query is widened to bf16 once (exact).
+//   The pages run QK on the MX-scaled fp4 x fp8 MFMA instead; measured on
+//   gfx950, that instruction rounds a 32-product block to ~14 bits relative
+//   to its largest product, which a saturated (+-448) query element turns
+//   into softmax errors beyond the parity bound, so the exact-product bf16
+//   MFMA with fp32 accumulation is used here. Tokens past the row's position
+//   are zeroed before the MFMA and masked after it, so NaN-poisoned tails
+//   never reach an accumulator.
+// * PV: O[head][d] += P[head][token] V[token][d] on v_mfma_f32_16x16x32_bf16.
+//   The QK result leaves each lane P for head n and tokens 4 kg + i of each
+//   16-token tile, which is directly a valid A operand once the k-step's token
+//   order is taken as {32 s + 4 kg + i, 32 s + 16 + 4 kg + i}. The output
+//   column order is permuted, d = 8 n + dt for d-tile dt, so that the B
+//   operand of lane (n, kg) needs, per token, the 8 consecutive codes
+//   d = 8 n .. 8 n + 7: one 4-byte load per token. Each byte widens to two
+//   bf16 (v_cvt_scalef32_pk_bf16_fp4 with the token's group scale) and a 2x2
+//   half-word transpose forms the MFMA operands; no LDS round trip.
+// * FP8 KV (e4m3 codes, per-token fp32 scale, bf16 query): QK on the bf16
+//   MFMA with the codes widened exactly to bf16 and the token scale applied to
+//   the dot product; PV folds the token scale into P.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mxs {
+
+constexpr int kAttnWaves = 4;
+
+__device__ __forceinline__ uint32_t lo_pair(uint32_t x, uint32_t y) { return (x & 0xFFFFu) | (y << 16); }
+__device__ __forceinline__ uint32_t hi_pair(uint32_t x, uint32_t y) { return (x >> 16) | (y & 0xFFFF0000u); }
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {   // fp32 -> bf16, round to nearest even
+  const uint32_t u = f2u(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// One block's operands as this lane loads them (all requested before any math).
+//  K: tile nt -> token 16 nt + n; MXFP4: 16 bytes of group kg + its scale byte;
+//     FP8: 32 bytes (elements 32 kg .. + 31) + 4 token scales (tokens 16 nt + 4 kg + i).
+//  V: k-step s -> the 8 tokens te(s, e); MXFP4: 4 bytes (codes 8 n .. 8 n + 7) per
+//     token + the scale dwords of the two 4-token runs; FP8: 8 bytes per token +
+//     the fp32 scales of the two runs.
+template <int FMT> struct BlockRegs;
+template <> struct BlockRegs<0> { u32x4 k[8]; uint32_t ks[8]; uint32_t v[4][8]; u32x4 vs[4][2]; };
+template <> struct BlockRegs<1> { u32x4 k[8][2]; f32x4 ks[8]; uint2 v[4][8]; f32x4 vs[4][2]; };
+
+// token of element e of the lane's k-group in PV k-step s
+__device__ __forceinline__ int pv_token(int s, int kg, int e) { return 32 * s + (e < 4 ? 4 * kg + e : 16 + 4 * kg + e - 4); }
+
+template <int FMT>
+__device__ __forceinline__ void load_block(BlockRegs<FMT> &r, const uint8_t *kp, const uint8_t *vp, int n, int kg) {
+  if constexpr (FMT == 0) {
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const int tok = 16 * nt + n;
+      r.k[nt] = *reinterpret_cast<const u32x4 *>(kp + 64 * tok + 16 * kg);
+      r.ks[nt] = kp[kMxScaleOff + 4 * tok + kg];
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r.v[s][e] = *reinterpret_cast<const uint32_t *>(vp + 64 * pv_token(s, kg, e) + 4 * n);
+      r.vs[s][0] = *reinterpret_cast<const u32x4 *>(vp + kMxScaleOff + 4 * pv_token(s, kg, 0));
+      r.vs[s][1] = *reinterpret_cast<const u32x4 *>(vp + kMxScaleOff + 4 * pv_token(s, kg, 4));
+    }
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const int tok = 16 * nt + n;
+      r.k[nt][0] = *reinterpret_cast<const u32x4 *>(kp + 128 * tok + 32 * kg);
+      r.k[nt][1] = *reinterpret_cast<const u32x4 *>(kp + 128 * tok + 32 * kg + 16);
+      r.ks[nt] = *reinterpret_cast<const f32x4 *>(kp + kF8ScaleOff + 4 * (16 * nt + 4 * kg));
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r.v[s][e] = *reinterpret_cast<const uint2 *>(vp + 128 * pv_token(s, kg, e) + 8 * n);
+      r.vs[s][0] = *reinterpret_cast<const f32x4 *>(vp + kF8ScaleOff + 4 * pv_token(s, kg, 0));
+      r.vs[s][1] = *reinterpret_cast<const f32x4 *>(vp + kF8ScaleOff + 4 * pv_token(s, kg, 4));
+    }
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void k_split_attn(CacheView c, const void *__restrict__ qv,
+                                                    const int32_t *__restrict__ block_table,
+                                                    int32_t q_rows, int32_t H, int32_t topk, int32_t P,
+                                                    float sm_scale, float *__restrict__ sp_m,
+                                                    float *__restrict__ sp_l, float *__restrict__ sp_o) {
+  __shared__ float s_m[kAttnWaves][16], s_l[kAttnWaves][16];
+  __shared__ float s_o[kAttnWaves][16][kDim + 4];
+  const int p = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int row = b * q_rows + j;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, kg = lane >> 4;
+  const int pos = c.context_lens[b] - q_rows + j;
+  const int cps = (topk + P - 1) / P;
+  const int slot0 = p * cps, slot1 = min(slot0 + cps, (int)topk);
+  const float NEG_INF = -__builtin_inff();
+
+  // B operand of QK: head n's query as bf16, elements 32 kg + 8 s .. + 7 for
+  // k-step s (the order of the key groups each lane loads). An e4m3 query is
+  // widened exactly; a bf16 query is loaded as is. Heads >= H load head 0 and
+  // are zeroed (unconditional loads).
+  bf16x8 qbf[4];
+  {
+    const int hq = n < H ? n : 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 v;
+      if constexpr (FMT == 0) {
+        const uint2 c8 = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint8_t *>(qv) +
+                                                          ((int64_t)row * H + hq) * kDim + 32 * kg + 8 * s);
+        const uint2 x = e4m3x4_to_bf16(c8.x), y = e4m3x4_to_bf16(c8.y);
+        v = u32x4{x.x, x.y, y.x, y.y};
+      } else {
+        v = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(qv) +
+                                             ((int64_t)row * H + hq) * kDim + 32 * kg + 8 * s);
+      }
+      if (n >= H) v = u32x4{0u, 0u, 0u, 0u};
+      qbf[s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  float m_run = NEG_INF, l_run = 0.0f;
+  f32x4 O[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int slot = slot0 + wave; slot < slot1; slot += kAttnWaves) {
+    const int blk = block_table[(int64_t)row * topk + slot];
+    if (blk < 0 || blk >= c.stride || blk * kTokens > pos) continue;
+    const int phys = c.page_table[(int64_t)b * c.stride + blk];
+    if (phys < 0 || phys >= c.num_pages) continue;
+    const int t0 = blk * kTokens;            // position of the page's first token
+    const int64_t pb = (int64_t)phys * (FMT == 0 ? kMxPageBytes : kF8PageBytes);
+    BlockRegs<FMT> r;
+    load_block<FMT>(r, c.k_pages + pb, c.v_pages + pb, n, kg);
+
+    // ---- QK: scores of tokens 16 nt + 4 kg + i for head n
+    float sc[8][4];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const bool live = t0 + 16 * nt + n <= pos;       // the lane's A row (token 16 nt + n)
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 a;
+        if constexpr (FMT == 0) {
+          uint32_t w4[4];
+          fp4x8_to_bf16(live ? r.k[nt][s] : 0u, e8m0_f32(live ? r.ks[nt] : 127u), w4);
+          a = u32x4{w4[0], w4[1], w4[2], w4[3]};
+        } else {
+          const u32x4 &src = r.k[nt][s >> 1];
+          const uint2 x = e4m3x4_to_bf16(live ? src[2 * (s & 1)] : 0u);
+          const uint2 y = e4m3x4_to_bf16(live ? src[2 * (s & 1) + 1] : 0u);
+          a = u32x4{x.x, x.y, y.x, y.y};
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qbf[s], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = acc[i] * sm_scale;
+        if constexpr (FMT == 1) x *= r.ks[nt][i];
+        sc[nt][i] = (t0 + 16 * nt + 4 * kg + i <= pos) ? x : NEG_INF;
+      }
+    }
+
+    // ---- online softmax for head n
+    float bm = NEG_INF;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bm = fmaxf(bm, sc[nt][i]);
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float m_new = fmaxf(m_run, bm);
+    const float alpha = __expf(m_run - m_new);      // 0 when m_run is -inf
+    float ps = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sc[nt][i] = __expf(sc[nt][i] - m_new);      // masked tokens: exp(-inf) = 0
+        ps += sc[nt][i];
+      }
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    // rescale O rows (heads 4 kg + i) by their head's alpha
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ai = __shfl(alpha, 4 * kg + i);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) O[dt][i] *= ai;
+    }
+
+    // ---- PV over 4 k-steps of 32 tokens
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 pa;                                     // P of the lane's 8 tokens as bf16
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        float p0 = sc[2 * s + (h >> 1)][2 * (h & 1)], p1 = sc[2 * s + (h >> 1)][2 * (h & 1) + 1];
+        if constexpr (FMT == 1) {
+          // fold V's token scale into P; masked tokens keep p = 0 (their scale may be NaN)
+          const f32x4 &vs = r.vs[s][h >> 1];
+          p0 = p0 == 0.0f ? 0.0f : p0 * vs[2 * (h & 1)];
+          p1 = p1 == 0.0f ? 0.0f : p1 * vs[2 * (h & 1) + 1];
+        }
+        pa[h] = bf16_bits_rne(p0) | (bf16_bits_rne(p1) << 16);
+      }
+      if constexpr (FMT == 0) {
+        uint32_t W[8][4];                           // token e, byte cb -> bf16 pair (d-tiles 2 cb, 2 cb + 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool live = t0 + pv_token(s, kg, e) <= pos;
+          const uint32_t sb = (r.vs[s][e >> 2][e & 3] >> (8 * (n >> 2))) & 0xFFu;
+          fp4x8_to_bf16(live ? r.v[s][e] : 0u, e8m0_f32(live ? sb : 127u), W[e]);
+        }
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          const u32x4 blo = {lo_pair(W[0][cb], W[1][cb]), lo_pair(W[2][cb], W[3][cb]), lo_pair(W[4][cb], W[5][cb]),
+                             lo_pair(W[6][cb], W[7][cb])};
+          const u32x4 bhi = {hi_pair(W[0][cb], W[1][cb]), hi_pair(W[2][cb], W[3][cb]), hi_pair(W[4][cb], W[5][cb]),
+                             hi_pair(W[6][cb], W[7][cb])};
+          O[2 * cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
+                                                              __builtin_bit_cast(bf16x8, blo), O[2 * cb], 0, 0, 0);
+          O[2 * cb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
+                                                                  __builtin_bit_cast(bf16x8, bhi), O[2 * cb + 1], 0, 0, 0);
+        }
+      } else {
+        uint32_t X0[8], X1[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool live = t0 + pv_token(s, kg, e) <= pos;
+          X0[e] = live ? r.v[s][e].x : 0u;
+          X1[e] = live ? r.v[s][e].y : 0u;
+        }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          u32x4 bv;
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const uint32_t ca = ((dt < 4 ? X0[2 * h] : X1[2 * h]) >> (8 * (dt & 3))) & 0xFFu;
+            const uint32_t cb = ((dt < 4 ? X0[2 * h + 1] : X1[2 * h + 1]) >> (8 * (dt & 3))) & 0xFFu;
+            bv[h] = e4m3_bf16_bits(ca) | (e4m3_bf16_bits(cb) << 16);
+          }
+          O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
+                                                          __builtin_bit_cast(bf16x8, bv), O[dt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- this wave's sums for head n, then the 4-wave merge through LDS
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (kg == 0) {
+    s_m[wave][n] = m_run;
+    s_l[wave][n] = l_run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * kg + i;
+    float M = NEG_INF;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    const float mine = s_m[wave][h];
+    const float f = (mine == NEG_INF) ? 0.0f : __expf(mine - M);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) s_o[wave][h][8 * n + dt] = O[dt][i] * f;
+  }
+  __syncthreads();
+  const int64_t part = (int64_t)row * H;      // + h, then * P + p
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) {
+    const int idx = threadIdx.x + 256 * rr;
+    const int h = idx >> 7, d = idx & 127;
+    if (h < H) {
+      float o = 0.f;
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) o += s_o[w][h][d];
+      sp_o[((part + h) * P + p) * kDim + d] = o;
+    }
+  }
+  if (threadIdx.x < (unsigned)H) {
+    const int h = threadIdx.x;
+    float M = NEG_INF;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    float Lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w)
+      Lsum += (s_m[w][h] == NEG_INF) ? 0.0f : s_l[w][h] * __expf(s_m[w][h] - M);
+    sp_m[(part + h) * P + p] = M;
+    sp_l[(part + h) * P + p] = Lsum;
+  }
+}
+
+hipError_t launch_split_attn(const CacheView &c, const void *q, int q_dtype, const int32_t *block_table,
+                             int32_t B, int32_t q_rows, int32_t H, int32_t topk, int32_t P, float sm_scale,
+                             float *sp_m, float *sp_l, float *sp_o, hipStream_t s) {
+  (void)q_dtype;
+  if (B * q_rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)P, (unsigned)q_rows, (unsigned)B);
+  if (c.kv_format == 0)
+    hipLaunchKernelGGL(k_split_attn<0>, grid, dim3(256), 0, s, c, q, block_table, q_rows, H, topk, P, sm_scale,
+                       sp_m, sp_l, sp_o);
+  else
+    hipLaunchKernelGGL(k_split_attn<1>, grid, dim3(256), 0, s, c, q, block_table, q_rows, H, topk, P, sm_scale,
+                       sp_m, sp_l, sp_o);
+  return hipGetLastError();
+}
+
+}  // namespace mxs

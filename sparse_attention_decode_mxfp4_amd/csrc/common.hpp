@@ -1,0 +1,124 @@
+// Device-side helpers shared by the mxsparse kernels (gfx950, wave64).
+//
+// Number formats (OCP Microscaling Formats v1.0 for e2m1 / e8m0, OCP FP8 for
+// e4m3; the pages name the formats, ATOM PR #2812 "Mono decode over the MXFP4
+// KV and index caches", commit messages):
+//   e2m1  1 sign, 2 exponent, 1 mantissa bit: +-{0, .5, 1, 1.5, 2, 3, 4, 6}
+//   e8m0  a power of two 2^(byte - 127); byte 255 is NaN
+//   e4m3  bias 7, max 448, 0x7F / 0xFF NaN, subnormals m * 2^-9
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxs {
+
+constexpr int kTokens = 128;           // tokens per page (= one block)
+constexpr int kDim = 128;              // head_dim
+constexpr int kMxPageBytes = 8704;     // 128 * 64 data + 128 * 4 scale bytes
+constexpr int kMxScaleOff = 8192;
+constexpr int kF8PageBytes = 16896;    // 128 * 128 codes + 128 fp32 scales
+constexpr int kF8ScaleOff = 16384;
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+__device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// ---------------------------------------------------------------- MXFP4 encode
+// e8m0 byte of a 32-element group from the fp32 bits of its largest magnitude:
+// OCP MX scale 2^(floor(log2 amax) - 2); floor(log2 amax) is the unbiased
+// exponent E - 127 of a normal amax, so the byte is E - 2, clamped at 0 (zero
+// and subnormal groups take the smallest scale).
+__device__ __forceinline__ uint32_t mx_scale_byte(uint32_t amax_bits) {
+  const uint32_t e = amax_bits >> 23;
+  return e > 2u ? e - 2u : 0u;
+}
+
+// 2^(127 - byte): multiplying by it divides by the group scale exactly
+// (byte <= 252 for finite input, so the factor stays a normal fp32).
+__device__ __forceinline__ float mx_inv_scale(uint32_t byte) { return u2f((254u - byte) << 23); }
+
+// e2m1 code of an already scaled value: nearest of {0, .5, 1, 1.5, 2, 3, 4, 6},
+// ties to the even code (0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2,
+// 3.5 -> 4, 5 -> 4), magnitudes above 6 saturate; sign bit 3 from the input.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = __builtin_fabsf(v);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return c | ((f2u(v) >> 28) & 8u);
+}
+
+// ---------------------------------------------------------------- e4m3 encode
+// Saturating OCP e4m3 code: round to nearest even, |x| >= 448 and inf -> 448,
+// NaN -> 0x7F, sign bit kept.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t u = f2u(x);
+  const uint32_t s = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return s | 0x7Fu;            // NaN
+  if (a >= 0x43E00000u) return s | 0x7Eu;           // >= 448, inf
+  if (a < 0x3C800000u) {                            // below 2^-6: grid m * 2^-9, m = 0..8
+    const float t = u2f(a) * 512.0f;                // exact scaling
+    return s | (uint32_t)__builtin_rintf(t);        // rint: round half to even
+  }
+  // normal: keep 3 mantissa bits, round half to even, rebias 127 -> 7
+  const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+  return s | (r - (120u << 3));
+}
+
+// ---------------------------------------------------------------- decode to bf16
+// fp32 value of the e8m0 scale byte, as the cvt_scalef32 instructions take it.
+__device__ __forceinline__ float e8m0_f32(uint32_t byte) {
+  return byte ? u2f(byte << 23) : u2f(0x00400000u);   // byte 0 is 2^-127 (an fp32 subnormal)
+}
+
+// Two e2m1 codes (byte `sel` of `packed`: low nibble first) times 2^(byte-127)
+// as two bf16 values; exact for every scale that keeps the result normal.
+#define MXS_CVT_FP4_BF16(packed, scale_f32, sel) \
+  __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((packed), (scale_f32), (sel))
+
+__device__ __forceinline__ uint32_t bf16x2_bits(bf16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// The four bytes of `packed` (8 e2m1 codes) as four bf16 pairs, scaled.
+__device__ __forceinline__ void fp4x8_to_bf16(uint32_t packed, float scale_f32, uint32_t out[4]) {
+  out[0] = bf16x2_bits(MXS_CVT_FP4_BF16(packed, scale_f32, 0));
+  out[1] = bf16x2_bits(MXS_CVT_FP4_BF16(packed, scale_f32, 1));
+  out[2] = bf16x2_bits(MXS_CVT_FP4_BF16(packed, scale_f32, 2));
+  out[3] = bf16x2_bits(MXS_CVT_FP4_BF16(packed, scale_f32, 3));
+}
+
+// e4m3 code -> bf16 bits (exact: e4m3 has 3 mantissa bits). Branch-free, so
+// that loads around it are not split by divergent control flow.
+__device__ __forceinline__ uint32_t e4m3_bf16_bits(uint32_t c) {
+  const uint32_t s = (c & 0x80u) << 8;
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const uint32_t normal = s | ((e + 120u) << 7) | (m << 4);
+  const uint32_t sub = s | (f2u((float)m * 0.001953125f) >> 16);     // m * 2^-9
+  const uint32_t r = e == 0u ? sub : normal;
+  return (c & 0x7Fu) == 0x7Fu ? (s | 0x7FC0u) : r;                   // 0x7F / 0xFF: NaN
+}
+
+// Four e4m3 codes (one dword) -> two dwords of bf16 pairs, element order kept.
+__device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t d) {
+  return make_uint2(e4m3_bf16_bits(d & 0xFFu) | (e4m3_bf16_bits((d >> 8) & 0xFFu) << 16),
+                    e4m3_bf16_bits((d >> 16) & 0xFFu) | (e4m3_bf16_bits(d >> 24) << 16));
+}
+
+// ---------------------------------------------------------------- wave helpers
+__device__ __forceinline__ float wave_max16(float v) {      // max over the 16 lanes sharing lane / 16
+  v = fmaxf(v, __shfl_xor(v, 1));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  v = fmaxf(v, __shfl_xor(v, 4));
+  v = fmaxf(v, __shfl_xor(v, 8));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63u; }
+
+}  // namespace mxs

@@ -1,0 +1,45 @@
+// Internal launchers between the C ABI (api.cpp) and the kernels. Arguments
+// are validated by the caller; launchers only size grids and enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxs {
+
+struct CacheView {
+  uint8_t *k_pages, *v_pages, *idx_pages;
+  int32_t num_pages, kv_format, idx_format;
+  const int32_t *page_table;
+  int32_t stride;
+  const int32_t *context_lens;
+};
+
+// row store / q store (store.hip)
+hipError_t launch_row_store(int format, const float *rows, int64_t n, const int64_t *slots,
+                            uint8_t *pages, int32_t num_pages, hipStream_t s);
+hipError_t launch_pack_q(const void *q, int q_dtype, int64_t n, uint8_t *q8, hipStream_t s);
+// the step's first kernel: new K / V / index rows into their slots, q -> e4m3
+hipError_t launch_step_store(const CacheView &c, const float *k_new, const float *v_new,
+                             const float *idx_new, int32_t B, int32_t q, const void *q_att,
+                             int q_dtype, int64_t q_elems, uint8_t *q8, hipStream_t s);
+
+// index scores (score.hip)
+hipError_t launch_index_score(const CacheView &c, const uint16_t *q_idx, const float *w, int32_t B,
+                              int32_t q, int32_t H_I, float *scores, hipStream_t s);
+
+// top-k (topk.hip)
+hipError_t launch_topk(const CacheView &c, const float *scores, int32_t B, int32_t q, int32_t topk,
+                       int32_t *block_table, hipStream_t s);
+
+// split attention (attn.hip)
+hipError_t launch_split_attn(const CacheView &c, const void *q, int q_dtype,
+                             const int32_t *block_table, int32_t B, int32_t q_rows, int32_t H,
+                             int32_t topk, int32_t P, float sm_scale, float *sp_m, float *sp_l,
+                             float *sp_o, hipStream_t s);
+
+// merge (merge.hip)
+hipError_t launch_lse_merge(const float *sp_m, const float *sp_l, const float *sp_o, int32_t n_rows,
+                            int32_t P, uint16_t *out, float *lse, hipStream_t s);
+
+}  // namespace mxs

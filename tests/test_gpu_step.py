@@ -1,0 +1,142 @@
+"""GPU parity of the whole decode step (decode_step through the C ABI) against
+the oracle's decode_step_ref: page bytes after the step's row store exact,
+top-k within the near-tie rule, output within the attention tolerance.
+
+Small workloads are checked on every sequence; the full-size ones (256K
+context, B = 32) in the launch configuration the bench times, on sampled
+sequences the oracle recomputes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import formats as OF
+from oracle import indexer as OI
+from oracle import step as OS
+from tests import parity as PT
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mx():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_decode_mxfp4_amd as m
+    m.lib()
+    return m
+
+
+def run_step(mx, inp, num_partitions=0):
+    import workloads.gpu as WG
+    wl = inp.wl
+    pools = WG.fill_prefix(inp, WG.empty_pools(inp))
+    cache = WG.make_cache(inp, pools)
+    t = WG.step_tensors(inp)
+    table = torch.empty((wl.B, wl.q, wl.topk), dtype=torch.int32, device="cuda")
+    scores = torch.empty((wl.B, wl.q, inp.max_pages), dtype=torch.float32, device="cuda")
+    step = mx.DecodeStep(cache, t["query"], t["q_idx"], t["w"], wl.topk, wl.sm_scale,
+                         k_new=t.get("k_new"), v_new=t.get("v_new"), idx_new=t.get("idx_new"),
+                         num_partitions=num_partitions, block_table_out=table, scores_out=scores)
+    step.run()
+    torch.cuda.synchronize()
+    return {"pools": {s: p.cpu().numpy() for s, p in pools.items()}, "table": table.cpu().numpy(),
+            "scores": scores.cpu().numpy().astype(np.float64), "O": step.out.float().cpu().numpy(),
+            "lse": step.lse.cpu().numpy()}
+
+
+def check_step(inp, g, seqs):
+    wl = inp.wl
+    r = OS.decode_step_ref(inp, seqs=seqs)
+    fmts = {"k": wl.kv_format, "v": wl.kv_format, "idx": wl.idx_format}
+    qa, _ = OS.attention_query(inp)
+    qI = OF.bf16_to_f64(inp.q_idx)
+    n_equal = n_rows = 0
+    for b in seqs:
+        L = int(inp.contexts[b])
+        pages = PT.seq_pages(inp.page_table[b], L)
+        for s, f in fmts.items():
+            PT.compare_pool_pages(g["pools"][s], r["pools"][s], pages, OF.PAGE_BYTES[f], f"{wl.name} {s} b={b}")
+        kI = OF.READ[wl.idx_format](r["pools"]["idx"], inp.page_table[b], L)
+        Sa = PT.score_bound(kI, qI[b], inp.w[b].astype(np.float64), L)
+        nc = OI.n_candidates(L, wl.q)
+        PT.check_scores(g["scores"][b], r["scores"][b][:, :Sa.shape[1]], Sa, nc)
+        same = []
+        for j in range(wl.q):
+            same.append(PT.check_topk(g["table"][b, j], r["block_table"][b, j], r["scores"][b, j], int(nc[j]),
+                                      wl.topk))
+        # attention over the GPU's own selection, every row
+        Oref, lref, _, _ = PT.oracle_attention_with_table(inp, r["pools"], qa, g["table"][b], b)
+        PT.check_attention(g["O"][b], Oref, f"{wl.name} b={b}")
+        np.testing.assert_allclose(g["lse"][b], lref, rtol=1e-4, atol=1e-4)
+        # end to end, on the rows whose selection equals the oracle's
+        for j in range(wl.q):
+            n_rows += 1
+            if same[j]:
+                n_equal += 1
+                PT.check_attention(g["O"][b, j], r["O"][b, j], f"{wl.name} b={b} j={j} end-to-end")
+    assert n_equal >= 0.9 * n_rows, f"only {n_equal}/{n_rows} rows select the oracle's exact set"
+
+
+@pytest.mark.parametrize("name", ["tiny", "fp8", "mxfp4_65k"])
+def test_decode_step_small(mx, name):
+    inp = W.make_inputs(W.WORKLOADS[name])
+    g = run_step(mx, inp)
+    check_step(inp, g, range(inp.wl.B))
+
+
+def test_decode_step_saturating_query(mx):
+    """The 65K workload with +-500 and +-inf injected into the query: the e4m3
+    store saturates them to +-448 and the step stays finite and in parity."""
+    inp = W.make_inputs(W.WORKLOADS["mxfp4_65k"], inject_q=True)
+    g = run_step(mx, inp)
+    check_step(inp, g, [0, 3])
+
+
+@pytest.mark.parametrize("P", [1, 64])
+def test_decode_step_partition_counts(mx, P):
+    inp = W.make_inputs(W.WORKLOADS["mxfp4_65k"].with_(B=2))
+    g = run_step(mx, inp, num_partitions=P)
+    check_step(inp, g, [0, 1])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(ctx_rule=("list", (9, 130, 1000, 4096)), B=4, q=8, H=16, topk=16),      # contexts near q, ragged
+    dict(ctx_rule=("list", (8, 300)), B=2, q=8, H=1, H_I=1, topk=64),            # L == q; H = 1; H_I = 1
+    dict(ctx_rule=("list", (5000, 3000)), B=2, q=16, H=7, H_I=3, topk=5),        # q = 16, odd head counts
+    dict(ctx_rule=("list", (2048,)), B=1, q=1, H=4, H_I=2, topk=16),             # top-k covers every block
+])
+def test_decode_step_edge_shapes(mx, kw):
+    wl = W.WORKLOADS["mxfp4_65k"].with_(name="edge", **kw)
+    inp = W.make_inputs(wl)
+    g = run_step(mx, inp)
+    check_step(inp, g, range(wl.B))
+
+
+def test_decode_step_empty_batch(mx):
+    import workloads.gpu as WG
+    inp = W.make_inputs(W.WORKLOADS["tiny"])
+    pools = WG.fill_prefix(inp, WG.empty_pools(inp))
+    cache = WG.make_cache(inp, pools)
+    t = WG.step_tensors(inp)
+    q0 = t["query"][:0]
+    step = mx.DecodeStep(cache, q0, t["q_idx"][:0], t["w"][:0], 4, 0.1)
+    step.run()
+    torch.cuda.synchronize()
+    assert step.out.numel() == 0
+
+
+@pytest.mark.parametrize("name,seqs", [("long", [0, 2]), ("headline", [1]), ("b32", [0, 17, 31])])
+def test_decode_step_full_size_sampled(mx, name, seqs):
+    inp = W.make_inputs(W.WORKLOADS[name])
+    g = run_step(mx, inp)
+    check_step(inp, g, seqs)
+    # every row of every sequence: finite output, a valid selection
+    assert np.isfinite(g["O"]).all()
+    for b in range(inp.wl.B):
+        nc = OI.n_candidates(int(inp.contexts[b]), inp.wl.q)
+        for j in range(inp.wl.q):
+            sel = g["table"][b, j]
+            k = min(inp.wl.topk, int(nc[j]))
+            assert (sel[:k] >= 0).all() and (np.diff(sel[:k]) > 0).all() and sel[k - 1] < nc[j]

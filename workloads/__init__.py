@@ -21,8 +21,8 @@ Workloads (the shapes of the pages' decode configurations, one TP rank's share):
 - ``headline`` B=4, q=8, MXFP4, every context 262144, top-k 32, full step.
 - ``b32``    B=32, q=8, MXFP4, ragged U[8192, 262144], top-k 32, full step.
 
-Values: K, V, index-K and q are N(0, 1) fp32; with ``outliers`` each element is
-multiplied by 20 with probability 1 %. Index queries are bf16 (fp32 N(0,1)
+Values: K, V, index-K and q are N(0, 1) fp32; with ``outliers`` about 1 % of
+the elements (Binomial(N, 0.01) uniformly drawn positions) are multiplied by 20. Index queries are bf16 (fp32 N(0,1)
 rounded to nearest even); index-head weights are U(0, 1) fp32.
 
 Pools: every cache pool starts filled with the byte 0xFF. In both cache formats
@@ -140,8 +140,9 @@ class StepInputs:
         rng = np.random.default_rng([self.wl.seed, _STREAM_OF[stream], b])
         x = rng.standard_normal((L, HEAD_DIM), dtype=np.float32)
         if self.wl.outliers:
-            m = rng.random((L, HEAD_DIM), dtype=np.float32) < 0.01
-            x[m] *= np.float32(20.0)
+            # Binomial(N, 1 %) element positions, drawn uniformly (a repeat is scaled once)
+            cnt = rng.binomial(L * HEAD_DIM, 0.01)
+            x.reshape(-1)[rng.integers(0, L * HEAD_DIM, size=cnt)] *= np.float32(20.0)
         return x
 
     def cache_rows(self, stream: str, b: int, keep: bool = False) -> np.ndarray:
