@@ -5,6 +5,8 @@
 Every HIP source is compiled with hipcc for gfx950 only. Packed fp32 VALU
 instructions are disabled (-packed-fp32-ops) and fp32 division and square
 root are correctly rounded (the FP8 row store divides by its per-token scale).
+MFMA results go to VGPRs (-amdgpu-mfma-vgpr-form): the kernels read every
+accumulator with VALU code, which AGPR results would first have to copy out.
 """
 from __future__ import annotations
 
@@ -26,6 +28,7 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

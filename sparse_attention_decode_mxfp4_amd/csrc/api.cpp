@@ -182,7 +182,8 @@ int index_score(const mxs_cache *cache, const uint16_t *q_idx, const float *w, i
   if (int r = check_score_args(cache, q_idx, w, B, q, H_I)) return r;
   REQ(scores && aligned(scores, 4), MXS_EINVAL, "scores: null or misaligned");
   if (B == 0) return ok();
-  return launched(mxs::launch_index_score(view(cache), q_idx, w, B, q, H_I, scores, (hipStream_t)stream),
+  return launched(mxs::launch_index_score(view(cache), q_idx, w, B, q, H_I, scores, mxs::StepStore{},
+                                          (hipStream_t)stream),
                   "index_score");
 }
 
@@ -222,7 +223,8 @@ int index_score_topk(const mxs_cache *cache, const uint16_t *q_idx, const float 
   REQ(aligned(sc, 4), MXS_EINVAL, "scores: misaligned");
   if (B == 0) return ok();
   const mxs::CacheView c = view(cache);
-  if (int r = launched(mxs::launch_index_score(c, q_idx, w, B, q, H_I, sc, (hipStream_t)stream), "index_score"))
+  if (int r = launched(mxs::launch_index_score(c, q_idx, w, B, q, H_I, sc, mxs::StepStore{}, (hipStream_t)stream),
+                       "index_score"))
     return r;
   return launched(mxs::launch_topk(c, sc, B, q, topk, block_table, (hipStream_t)stream), "topk_blocks");
 }
@@ -329,18 +331,27 @@ int decode_step(const mxs_step *a, void *ws, size_t ws_bytes, void *stream) {
   float *sp_o = reinterpret_cast<float *>(base + w.sp_o);
   const hipStream_t s = (hipStream_t)stream;
   const mxs::CacheView c = view(cache);
-  const int64_t q_elems = (int64_t)a->B * a->q * a->H * MXS_HEAD_DIM;
 
-  // 1 + 2: new rows into the pages, q -> e4m3 (one launch)
-  if (store || mx) {
-    if (int r = launched(mxs::launch_step_store(c, a->k_new, a->v_new, a->idx_new, store ? a->B : 0, a->q, a->query,
-                                                a->q_dtype, mx ? q_elems : 0, mx ? q8 : nullptr, s),
-                         "decode_step: store"))
-      return r;
+  // 1 - 3: the new rows into the pages, q -> e4m3 and the scores, one launch
+  // (the waves that own a page holding new positions store those index rows
+  // before scoring it; K / V rows and q are read only by the attention
+  // launch)
+  mxs::StepStore st;
+  if (store) {
+    st.k_new = a->k_new;
+    st.v_new = a->v_new;
+    st.idx_new = a->idx_new;
   }
-  // 3 + 4: scores, top-k
-  if (int r = launched(mxs::launch_index_score(c, a->q_idx, a->w, a->B, a->q, a->H_I, scores, s), "decode_step: score"))
+  if (mx) {
+    st.q_att = a->query;
+    st.q_dtype = a->q_dtype;
+    st.H = a->H;
+    st.q8 = q8;
+  }
+  if (int r = launched(mxs::launch_index_score(c, a->q_idx, a->w, a->B, a->q, a->H_I, scores, st, s),
+                       "decode_step: store + score"))
     return r;
+  // 4: top-k
   if (int r = launched(mxs::launch_topk(c, scores, a->B, a->q, a->topk, table, s), "decode_step: topk")) return r;
   // 5: split attention, 6: merge
   const void *qa = mx ? static_cast<const void *>(q8) : a->query;

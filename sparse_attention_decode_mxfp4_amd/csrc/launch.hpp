@@ -19,14 +19,20 @@ struct CacheView {
 hipError_t launch_row_store(int format, const float *rows, int64_t n, const int64_t *slots,
                             uint8_t *pages, int32_t num_pages, hipStream_t s);
 hipError_t launch_pack_q(const void *q, int q_dtype, int64_t n, uint8_t *q8, hipStream_t s);
-// the step's first kernel: new K / V / index rows into their slots, q -> e4m3
-hipError_t launch_step_store(const CacheView &c, const float *k_new, const float *v_new,
-                             const float *idx_new, int32_t B, int32_t q, const void *q_att,
-                             int q_dtype, int64_t q_elems, uint8_t *q8, hipStream_t s);
+
+// The decode step's own stores, done inside the scorer launch (all null: none):
+// the new K / V / index rows [B][q][128] fp32 (row j of sequence b goes to
+// position L_b - q + j) and the query packed to e4m3 (q8 non-null).
+struct StepStore {
+  const float *k_new = nullptr, *v_new = nullptr, *idx_new = nullptr;
+  const void *q_att = nullptr;
+  int q_dtype = 0, H = 0;
+  uint8_t *q8 = nullptr;
+};
 
 // index scores (score.hip)
 hipError_t launch_index_score(const CacheView &c, const uint16_t *q_idx, const float *w, int32_t B,
-                              int32_t q, int32_t H_I, float *scores, hipStream_t s);
+                              int32_t q, int32_t H_I, float *scores, const StepStore &st, hipStream_t s);
 
 // top-k (topk.hip)
 hipError_t launch_topk(const CacheView &c, const float *scores, int32_t B, int32_t q, int32_t topk,

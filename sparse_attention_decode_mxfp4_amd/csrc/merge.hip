@@ -1,12 +1,9 @@
-// Log-sum-exp merge of the split partials (ATOM PR #2812, "Mono decode over the
-// MXFP4 KV and index caches", commit message of the MXFP4 main-KV commit: the
-// merge consumes sp_o / sp_m / sp_l).
-//   M = max_p m_p;  L = sum_p l_p e^(m_p - M);  O = sum_p o_p e^(m_p - M) / L;
-//   lse = M + ln L.  Empty partitions (m_p = -inf) weigh nothing.
-// One wave per (query row, head): lane p < P reads partition p's (m, l); each
-// lane owns two output elements.
+// Stand-alone log-sum-exp merge of split partials: one wave per (query row,
+// head); the arithmetic is merge_one (merge.hpp). The decode step merges
+// inside its attention launch instead.
 #include "common.hpp"
 #include "launch.hpp"
+#include "merge.hpp"
 
 namespace mxs {
 
@@ -14,42 +11,8 @@ __global__ __launch_bounds__(256) void k_lse_merge(const float *__restrict__ sp_
                                                    const float *__restrict__ sp_o, int32_t n_rows, int32_t P,
                                                    uint16_t *__restrict__ out, float *__restrict__ lse) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
   if (r >= n_rows) return;
-  const float NEG_INF = -__builtin_inff();
-  const float mraw = sp_m[(int64_t)r * P + min(lane, P - 1)];
-  const float lraw = sp_l[(int64_t)r * P + min(lane, P - 1)];
-  const float mp = lane < P ? mraw : NEG_INF;
-  float M = mp;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
-  const float wp = (lane < P && mp != NEG_INF) ? __expf(mp - M) : 0.0f;
-  float Lp = lane < P ? lraw * wp : 0.0f;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) Lp += __shfl_xor(Lp, o);
-  const float inv = Lp > 0.0f ? 1.0f / Lp : 0.0f;
-  float a0 = 0.f, a1 = 0.f;
-  const float2 *po = reinterpret_cast<const float2 *>(sp_o + (int64_t)r * P * kDim) + lane;
-  for (int p0 = 0; p0 < P; p0 += 8) {           // 8 partitions' loads in flight at once
-    float2 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = po[min(p0 + u, P - 1) * (kDim / 2)];   // clamped: no branch
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float wq = __shfl(wp, p0 + u < P ? p0 + u : 0);
-      if (p0 + u < P && wq != 0.0f) {
-        a0 += wq * v[u].x;
-        a1 += wq * v[u].y;
-      }
-    }
-  }
-  a0 *= inv;
-  a1 *= inv;
-  const uint32_t u0 = f2u(a0), u1 = f2u(a1);
-  const uint32_t b0 = (u0 + 0x7FFFu + ((u0 >> 16) & 1u)) >> 16;   // round to nearest even
-  const uint32_t b1 = (u1 + 0x7FFFu + ((u1 >> 16) & 1u)) >> 16;
-  reinterpret_cast<uint32_t *>(out + (int64_t)r * kDim)[lane] = b0 | (b1 << 16);
-  if (lse && lane == 0) lse[r] = Lp > 0.0f ? M + __logf(Lp) : NEG_INF;
+  merge_one(sp_m, sp_l, sp_o, r, P, threadIdx.x & 63, out, lse);
 }
 
 hipError_t launch_lse_merge(const float *sp_m, const float *sp_l, const float *sp_o, int32_t n_rows, int32_t P,

@@ -1,0 +1,71 @@
+// Row store and q store device functions, shared by the stand-alone store
+// kernels and the index scorer (which stores the step's new rows itself).
+//
+// ATOM PR #2812, "Mono decode over the MXFP4 KV and index caches": the
+// MXFP4 index-cache commit writes each index-key row into an 8704 B page
+// (e8m0 group scale, e2m1 elements), the main-KV commit writes K and V rows
+// with the same row store, and the e4m3 q-store commit packs the query to
+// e4m3 with unit scale, saturating.
+//
+// One wave stores one 128-element row: lane l owns elements 2l and 2l+1, so a
+// 32-element group is 16 lanes and its amax is a 16-lane reduction; the wave
+// writes the row's 64 data bytes (one per lane) and one dword of 4 scales.
+#pragma once
+
+#include "common.hpp"
+
+namespace mxs {
+
+// Quantize one fp32 row (this wave's lane owns x = elements 2l, 2l+1) into
+// token `tok` of the MXFP4 page at `page`.
+__device__ __forceinline__ void mx_store_row(float2 x, uint8_t *page, int tok, int lane) {
+  uint32_t a = max(f2u(x.x) & 0x7FFFFFFFu, f2u(x.y) & 0x7FFFFFFFu);   // |.| bits order like values
+  a = max(a, (uint32_t)__shfl_xor((int)a, 1));
+  a = max(a, (uint32_t)__shfl_xor((int)a, 2));
+  a = max(a, (uint32_t)__shfl_xor((int)a, 4));
+  a = max(a, (uint32_t)__shfl_xor((int)a, 8));
+  const uint32_t sb = mx_scale_byte(a);
+  const float inv = mx_inv_scale(sb);
+  const uint32_t c0 = e2m1_code(x.x * inv);
+  const uint32_t c1 = e2m1_code(x.y * inv);
+  page[64 * tok + lane] = (uint8_t)(c0 | (c1 << 4));
+  const uint32_t s1 = (uint32_t)__shfl((int)sb, 16);
+  const uint32_t s2 = (uint32_t)__shfl((int)sb, 32);
+  const uint32_t s3 = (uint32_t)__shfl((int)sb, 48);
+  if (lane == 0)
+    *reinterpret_cast<uint32_t *>(page + kMxScaleOff + 4 * tok) = sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
+}
+
+// FP8 per-token row: scale = fp32(amax / 448) (1 for an all-zero row),
+// code = e4m3(fp32(x / scale)); IEEE division on both.
+__device__ __forceinline__ void f8_store_row(float2 x, uint8_t *page, int tok, int lane) {
+  uint32_t a = max(f2u(x.x) & 0x7FFFFFFFu, f2u(x.y) & 0x7FFFFFFFu);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) a = max(a, (uint32_t)__shfl_xor((int)a, o));
+  const float amax = u2f(a);
+  const float scale = amax == 0.0f ? 1.0f : amax / 448.0f;
+  const uint32_t c0 = e4m3_code(x.x / scale);
+  const uint32_t c1 = e4m3_code(x.y / scale);
+  *reinterpret_cast<uint16_t *>(page + 128 * tok + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
+  if (lane == 0) *reinterpret_cast<float *>(page + kF8ScaleOff + 4 * tok) = scale;
+}
+
+__device__ __forceinline__ float load_q_elem(const void *q, int q_dtype, int64_t i) {
+  if (q_dtype == 1) return u2f((uint32_t)reinterpret_cast<const uint16_t *>(q)[i] << 16);
+  return reinterpret_cast<const float *>(q)[i];
+}
+
+// Four consecutive elements per thread.
+__device__ __forceinline__ void pack_q4(const void *q, int q_dtype, int64_t n, uint8_t *q8, int64_t i) {
+  if (i >= n) return;
+  if (i + 4 <= n && ((reinterpret_cast<uintptr_t>(q8) + i) & 3) == 0) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w |= e4m3_code(load_q_elem(q, q_dtype, i + e)) << (8 * e);
+    *reinterpret_cast<uint32_t *>(q8 + i) = w;
+  } else {
+    for (int e = 0; e < 4 && i + e < n; ++e) q8[i + e] = (uint8_t)e4m3_code(load_q_elem(q, q_dtype, i + e));
+  }
+}
+
+}  // namespace mxs

@@ -25,27 +25,68 @@
 // in the lane, and the block max is a 16-lane reduction per page.
 #include "common.hpp"
 #include "launch.hpp"
+#include "rowstore.hpp"
 
 namespace mxs {
-
-constexpr int kScoreWaves = 4;     // waves per workgroup
-constexpr int kPagesPerWave = 2;   // pages each wave scores, in half-page chunks
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 typedef __attribute__((address_space(1))) void *glb_ptr_t;
 
-// Chunk staging. A chunk is half a page (64 tokens). Each wave owns two LDS
-// stages of one chunk and pipelines them: chunk u + 1 is copied global -> LDS
-// with the direct-to-LDS loads (global_load_lds_dwordx4: 64 lanes x 16 B land
-// in 1 KiB of LDS in lane order; nothing is held in VGPRs) while chunk u is
-// computed. Each lane reads back exactly the bytes it copied. Lane (n, kg) of
-// the chunk's tile nt (token 64 h + 16 nt + n of the page, h = half):
+// Chunk staging. A chunk is half a page (64 tokens). Each wave owns a ring of
+// S LDS stages and keeps S - 1 chunks in flight: chunk u + S - 1 is copied
+// global -> LDS with the direct-to-LDS loads (global_load_lds_dwordx4: 64
+// lanes x 16 B land in 1 KiB of LDS in lane order; nothing is held in VGPRs)
+// while chunk u is computed. Each lane reads back exactly the bytes it copied.
+// Lane (n, kg) of the chunk's tile nt (token 64 h + 16 nt + n of the page,
+// h = half):
 //   MXFP4: codes of group kg (16 B) at stage + 1024 nt + 16 lane;
 //   FP8:   codes 32 kg .. 32 kg + 31 (2 x 16 B) at stage + 1024 (2 nt + c) + 16 lane.
 // The chunk's 256 B of per-token scales follow the codes (4096 or 8192 B in).
 template <int FMT> struct Chunk;
 template <> struct Chunk<0> { static constexpr int kCodes = 4096, kBytes = 4096 + 256, kDma = 5, kPage = kMxPageBytes, kScale = kMxScaleOff; };
 template <> struct Chunk<1> { static constexpr int kCodes = 8192, kBytes = 8192 + 256, kDma = 9, kPage = kF8PageBytes, kScale = kF8ScaleOff; };
+
+// Launch shape per index format: waves per workgroup, pages per wave, LDS
+// stages per wave. MXFP4: 4 x 4 x 4 stages of 4.25 KiB = 68 KiB of LDS per
+// workgroup, two workgroups per CU, ~100 KiB of copies in flight per CU.
+template <int FMT> struct ScoreShape;
+template <> struct ScoreShape<0> { static constexpr int kWaves = 4, kPages = 4, kStages = 4; };
+template <> struct ScoreShape<1> { static constexpr int kWaves = 4, kPages = 2, kStages = 2; };
+
+// s_waitcnt vmcnt(n * D) for a wave-uniform n <= K that is a constant once the
+// chunk loop is unrolled: at most the n most recently issued chunks (D copies
+// each) still in flight.
+template <int D, int K>
+__device__ __forceinline__ void wait_chunks(int n) {
+  if constexpr (K == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    if (n >= K)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K * D) : "memory");
+    else
+      wait_chunks<D, K - 1>(n);
+  }
+}
+
+// max(x, 0) as one integer max on the bits: a negative float is a negative
+// int (-> +0), any other value keeps its bits. Unlike fmaxf on an MFMA result
+// it needs no NaN canonicalisation in front.
+__device__ __forceinline__ float relu1(float x) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
+// max over the 16 lanes sharing lane / 16, through DPP lane swizzles (no LDS):
+// xor 1 and xor 2 within a quad, then the half-row and row mirrors
+template <int CTRL>
+__device__ __forceinline__ float dpp_swizzle(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float max16_dpp(float v) {
+  v = fmaxf(v, dpp_swizzle<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_swizzle<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_swizzle<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, dpp_swizzle<0x140>(v));   // row_mirror
+  return v;
+}
 
 template <int FMT>
 __device__ __forceinline__ void dma_chunk(uint8_t *stage, const uint8_t *page, int h, int n, int kg, int lane) {
@@ -94,38 +135,60 @@ __device__ __forceinline__ void key_operands(const uint8_t *stage, int nt, int n
   }
 }
 
-template <int MT, int FMT>
-__global__ __launch_bounds__(64 * kScoreWaves) void k_index_score(CacheView c, const uint16_t *__restrict__ q_idx,
-                                                                  const float *__restrict__ w, int32_t q,
-                                                                  int32_t H_I, float *__restrict__ scores) {
+// The decode step's K / V row stores and q pack for sequence b, spread over
+// the sequence's NW-wave workgroups (nothing in this launch reads them; the
+// attention launch that follows does): row r of the 2q K / V rows goes to wave
+// r of the sequence's waves, q element 4i to thread i.
+template <int NW>
+__device__ __forceinline__ void step_side_stores(const CacheView &c, const StepStore &st, int b, int q, int L,
+                                                 int lane, int wave) {
+  const int nwg = gridDim.x;
+  if (st.k_new) {
+    for (int r = blockIdx.x * NW + wave; r < 2 * q; r += nwg * NW) {
+      const int j = r % q, t = L - q + j;
+      if (t < 0 || t / kTokens >= c.stride) continue;
+      const int page = c.page_table[(int64_t)b * c.stride + t / kTokens];
+      if (page < 0 || page >= c.num_pages) continue;
+      const float *src = (r < q ? st.k_new : st.v_new) + ((int64_t)b * q + j) * kDim;
+      uint8_t *pool = r < q ? c.k_pages : c.v_pages;
+      const float2 x = reinterpret_cast<const float2 *>(src)[lane];
+      if (c.kv_format == 0)
+        mx_store_row(x, pool + (int64_t)page * kMxPageBytes, t % kTokens, lane);
+      else
+        f8_store_row(x, pool + (int64_t)page * kF8PageBytes, t % kTokens, lane);
+    }
+  }
+  if (st.q8) {
+    const int64_t n = (int64_t)q * st.H * kDim, base = (int64_t)b * n;
+    for (int64_t i = 4 * ((int64_t)blockIdx.x * 64 * NW + threadIdx.x); i < n; i += 4 * (int64_t)nwg * 64 * NW)
+      pack_q4(st.q_att, st.q_dtype, base + n, st.q8, base + i);
+  }
+}
+
+template <int MT, int FMT, int NW, int PPW, int S>
+__global__ __launch_bounds__(64 * NW) void k_index_score(CacheView c, const uint16_t *__restrict__ q_idx,
+                                                         const float *__restrict__ w, int32_t q, int32_t H_I,
+                                                         float *__restrict__ scores, StepStore st) {
   using CK = Chunk<FMT>;
-  __shared__ __attribute__((aligned(16))) uint8_t stages[kScoreWaves][2][CK::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t stages[NW][S][CK::kBytes];
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, kg = lane >> 4;
-  const int p0 = (blockIdx.x * kScoreWaves + wave) * kPagesPerWave;
-  if (p0 >= c.stride) return;
-  const int L = c.context_lens[b];
-  const int lim = min((L + kTokens - 1) / kTokens, (int)c.stride);    // pages holding tokens
+  const int p0 = (blockIdx.x * NW + wave) * PPW;
   const float NEG_INF = -__builtin_inff();
   float *srow = scores + (int64_t)b * q * c.stride;
-  if (p0 >= lim) {                                  // past the context: no candidates here
-    for (int i = 0; i < kPagesPerWave && p0 + i < c.stride; ++i)
-      if (n == 0)
-        for (int jw = kg; jw < q; jw += 4) srow[(int64_t)jw * c.stride + p0 + i] = NEG_INF;
+  if (p0 >= c.stride) {                             // the grid's rounding: no pages
+    step_side_stores<NW>(c, st, b, q, c.context_lens[b], lane, wave);
     return;
   }
 
-  // page ids of this wave's pages, all requested at once (clamped, so the
-  // loads are unconditional); invalid entries read page 0 and are masked
-  int phys[kPagesPerWave];
-  bool valid[kPagesPerWave];
+  // ---- prologue, one round trip: the context length, this wave's page ids
+  // (clamped to the table row, so every load is unconditional; entries past
+  // the context or out of range are masked below), the A operand and weights.
+  const int L = c.context_lens[b];
+  int raw[PPW];
 #pragma unroll
-  for (int i = 0; i < kPagesPerWave; ++i) {
-    const int raw = c.page_table[(int64_t)b * c.stride + min(p0 + i, lim - 1)];
-    valid[i] = p0 + i < lim && raw >= 0 && raw < c.num_pages;
-    phys[i] = valid[i] ? raw : 0;
-  }
+  for (int i = 0; i < PPW; ++i) raw[i] = c.page_table[(int64_t)b * c.stride + min(p0 + i, c.stride - 1)];
 
   // A operand: q_idx rows m = 16 mt + n -> (query row m / 4, head m % 4); rows
   // past q or H_I are zero (their load reads row 0 and is discarded)
@@ -144,11 +207,9 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_index_score(CacheView c, c
   }
   // result rows 16 mt + 4 kg + i -> query row 4 mt + kg, index head i
   float wv[MT][4];
-  int posw[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int jw = 4 * mt + kg;
-    posw[mt] = L - q + jw;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool ok = jw < q && i < H_I;
@@ -156,7 +217,6 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_index_score(CacheView c, c
       wv[mt][i] = ok ? x : 0.0f;
     }
   }
-
   // Consume every prologue load here, so that no compiler-placed wait for them
   // lands inside the chunk pipeline (the compiler does not count the
   // direct-to-LDS copies and would wait for all of them).
@@ -168,32 +228,80 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_index_score(CacheView c, c
     for (int s = 0; s < 4; ++s) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, A[mt][s])));
   }
 #pragma unroll
-  for (int i = 0; i < kPagesPerWave; ++i) asm volatile("" ::"v"(phys[i]));
-  asm volatile("" ::: "memory");
+  for (int i = 0; i < PPW; ++i) asm volatile("" ::"v"(raw[i]));
+  asm volatile("" ::"s"(L) : "memory");
 
-  // The waits are explicit (the compiler does not order LDS reads after
-  // direct-to-LDS loads): vmcnt counts this wave's vector memory operations in
-  // issue order, so "at most kDma outstanding" right after issuing chunk u + 1
-  // means every older operation — chunk u's copies included — is done.
-  constexpr int kUnits = 2 * kPagesPerWave;
-  dma_chunk<FMT>(stages[wave][0], c.idx_pages + (int64_t)phys[0] * CK::kPage, 0, n, kg, lane);
+  const int lim = min((L + kTokens - 1) / kTokens, (int)c.stride);    // pages holding tokens
+  if (p0 >= lim) {                                  // past the context: no candidates here
+    for (int i = 0; i < PPW && p0 + i < c.stride; ++i)
+      if (n == 0)
+        for (int jw = kg; jw < q; jw += 4) srow[(int64_t)jw * c.stride + p0 + i] = NEG_INF;
+    step_side_stores<NW>(c, st, b, q, L, lane, wave);
+    return;
+  }
+  int phys[PPW];
+  bool valid[PPW];
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) {
+    valid[i] = p0 + i < lim && raw[i] >= 0 && raw[i] < c.num_pages;
+    phys[i] = valid[i] ? raw[i] : 0;
+  }
+  int posw[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) posw[mt] = L - q + 4 * mt + kg;
+  const int pos_min = L - q;                        // the first query row's position
+
+  // The step's new index rows that fall in this wave's pages are stored here,
+  // before the pages are copied; the wave waits for its own stores, which
+  // reach L2 before the copies read it (nothing cached them earlier).
+  if (st.idx_new && L - 1 >= p0 * kTokens && L - q < (p0 + PPW) * kTokens) {
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+      if (!valid[i]) continue;
+      for (int j = 0; j < q; ++j) {
+        const int t = L - q + j;
+        if (t < 0 || t / kTokens != p0 + i) continue;
+        const float2 x = reinterpret_cast<const float2 *>(st.idx_new + ((int64_t)b * q + j) * kDim)[lane];
+        if constexpr (FMT == 0)
+          mx_store_row(x, c.idx_pages + (int64_t)phys[i] * kMxPageBytes, t % kTokens, lane);
+        else
+          f8_store_row(x, c.idx_pages + (int64_t)phys[i] * kF8PageBytes, t % kTokens, lane);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
+  // ---- the chunk pipeline. The waits are explicit (the compiler does not
+  // order LDS reads after direct-to-LDS loads): vmcnt counts this wave's
+  // vector memory operations in issue order, so "at most n chunks' copies
+  // outstanding" right after issuing chunk u + n means every older operation
+  // — chunk u's copies included — is done (younger stores only make the wait
+  // longer). Stage (u + S - 1) % S is refilled only after chunk u - 1, which
+  // it held, has been computed.
+  constexpr int kUnits = 2 * PPW;
+#pragma unroll
+  for (int u = 0; u < S - 1 && u < kUnits; ++u)
+    dma_chunk<FMT>(stages[wave][u], c.idx_pages + (int64_t)phys[u >> 1] * CK::kPage, u & 1, n, kg, lane);
+  // the side stores go out while the first copies are in flight
+  step_side_stores<NW>(c, st, b, q, L, lane, wave);
+
   float rmax[MT];
 #pragma unroll
   for (int u = 0; u < kUnits; ++u) {
     const int i = u >> 1, h = u & 1;
     const int p = p0 + i;
-    const uint8_t *stage = stages[wave][u & 1];
-    if (u + 1 < kUnits) {
-      dma_chunk<FMT>(stages[wave][(u + 1) & 1], c.idx_pages + (int64_t)phys[(u + 1) >> 1] * CK::kPage, (u + 1) & 1,
-                     n, kg, lane);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CK::kDma) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint8_t *stage = stages[wave][u % S];
+    if (u + S - 1 < kUnits) {
+      const int un = u + S - 1;
+      dma_chunk<FMT>(stages[wave][un % S], c.idx_pages + (int64_t)phys[un >> 1] * CK::kPage, un & 1, n, kg, lane);
     }
+    wait_chunks<CK::kDma, S - 1>(min(S - 1, kUnits - 1 - u));
     if (h == 0) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) rmax[mt] = NEG_INF;
     }
+    // tokens of this chunk all at or before every row's position: no mask
+    const bool full = p * kTokens + 64 * h + 63 <= pos_min;
 #pragma unroll 2
     for (int nt = 0; nt < 4; ++nt) {
       bf16x8 Bk[4];
@@ -207,41 +315,47 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_index_score(CacheView c, c
         for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][s], Bk[s], acc, 0, 0, 0);
         float v = 0.f;
 #pragma unroll
-        for (int hd = 0; hd < 4; ++hd) v += wv[mt][hd] * fmaxf(FMT == 1 ? acc[hd] * ksc : acc[hd], 0.0f);
-        rmax[mt] = fmaxf(rmax[mt], t <= posw[mt] ? v : NEG_INF);
+        for (int hd = 0; hd < 4; ++hd) v += wv[mt][hd] * relu1(FMT == 1 ? acc[hd] * ksc : acc[hd]);
+        rmax[mt] = fmaxf(rmax[mt], (full || t <= posw[mt]) ? v : NEG_INF);
       }
     }
-    if (h == 1 && p < c.stride) {
+    if (h == 1) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const float r = wave_max16(rmax[mt]);
+        const float r = max16_dpp(rmax[mt]);
         const int jw = 4 * mt + kg;
-        if (n == 0 && jw < q) srow[(int64_t)jw * c.stride + p] = valid[i] ? r : NEG_INF;
+        if (n == 0 && jw < q && p < c.stride) srow[(int64_t)jw * c.stride + p] = valid[i] ? r : NEG_INF;
       }
     }
   }
+}
+
+template <int FMT, int MT>
+static void launch_shape(const CacheView &c, const uint16_t *q_idx, const float *w, int32_t B, int32_t q,
+                         int32_t H_I, float *scores, const StepStore &st, hipStream_t s) {
+  using SH = ScoreShape<FMT>;
+  const dim3 grid((unsigned)((c.stride + SH::kWaves * SH::kPages - 1) / (SH::kWaves * SH::kPages)), (unsigned)B);
+  hipLaunchKernelGGL((k_index_score<MT, FMT, SH::kWaves, SH::kPages, SH::kStages>), grid, dim3(64 * SH::kWaves), 0,
+                     s, c, q_idx, w, q, H_I, scores, st);
 }
 
 template <int FMT>
 static void launch_fmt(const CacheView &c, const uint16_t *q_idx, const float *w, int32_t B, int32_t q,
-                       int32_t H_I, float *scores, hipStream_t s) {
-  const dim3 grid((unsigned)((c.stride + kScoreWaves * kPagesPerWave - 1) / (kScoreWaves * kPagesPerWave)),
-                  (unsigned)B);
-  const int mt = (4 * q + 15) / 16;
-  switch (mt) {
-    case 1: hipLaunchKernelGGL((k_index_score<1, FMT>), grid, dim3(256), 0, s, c, q_idx, w, q, H_I, scores); break;
-    case 2: hipLaunchKernelGGL((k_index_score<2, FMT>), grid, dim3(256), 0, s, c, q_idx, w, q, H_I, scores); break;
-    case 3: hipLaunchKernelGGL((k_index_score<3, FMT>), grid, dim3(256), 0, s, c, q_idx, w, q, H_I, scores); break;
-    default: hipLaunchKernelGGL((k_index_score<4, FMT>), grid, dim3(256), 0, s, c, q_idx, w, q, H_I, scores); break;
+                       int32_t H_I, float *scores, const StepStore &st, hipStream_t s) {
+  switch ((4 * q + 15) / 16) {                      // M tiles: 4 A-rows per query row
+    case 1: launch_shape<FMT, 1>(c, q_idx, w, B, q, H_I, scores, st, s); break;
+    case 2: launch_shape<FMT, 2>(c, q_idx, w, B, q, H_I, scores, st, s); break;
+    case 3: launch_shape<FMT, 3>(c, q_idx, w, B, q, H_I, scores, st, s); break;
+    default: launch_shape<FMT, 4>(c, q_idx, w, B, q, H_I, scores, st, s); break;
   }
 }
 
 hipError_t launch_index_score(const CacheView &c, const uint16_t *q_idx, const float *w, int32_t B,
-                              int32_t q, int32_t H_I, float *scores, hipStream_t s) {
+                              int32_t q, int32_t H_I, float *scores, const StepStore &st, hipStream_t s) {
   if (c.idx_format == 0)
-    launch_fmt<0>(c, q_idx, w, B, q, H_I, scores, s);
+    launch_fmt<0>(c, q_idx, w, B, q, H_I, scores, st, s);
   else
-    launch_fmt<1>(c, q_idx, w, B, q, H_I, scores, s);
+    launch_fmt<1>(c, q_idx, w, B, q, H_I, scores, st, s);
   return hipGetLastError();
 }
 
