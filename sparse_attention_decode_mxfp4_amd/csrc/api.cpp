@@ -351,14 +351,15 @@ int decode_step(const mxs_step *a, void *ws, size_t ws_bytes, void *stream) {
   if (int r = launched(mxs::launch_index_score(c, a->q_idx, a->w, a->B, a->q, a->H_I, scores, st, s),
                        "decode_step: store + score"))
     return r;
-  // 4: top-k
-  if (int r = launched(mxs::launch_topk(c, scores, a->B, a->q, a->topk, table, s), "decode_step: topk")) return r;
-  // 5: split attention, 6: merge
+  // 4 + 5: top-k and split attention, one launch: every attention workgroup
+  // selects its row's blocks from the scores itself (partition 0 writes the
+  // row's block table)
   const void *qa = mx ? static_cast<const void *>(q8) : a->query;
-  if (int r = launched(mxs::launch_split_attn(c, qa, mx ? MXS_E4M3 : MXS_BF16, table, a->B, a->q, a->H, a->topk, P,
-                                              a->sm_scale, sp_m, sp_l, sp_o, s),
-                       "decode_step: split attention"))
+  if (int r = launched(mxs::launch_select_attn(c, scores, qa, a->B, a->q, a->H, a->topk, P, a->sm_scale, table, sp_m,
+                                               sp_l, sp_o, s),
+                       "decode_step: top-k + split attention"))
     return r;
+  // 6: merge
   return launched(mxs::launch_lse_merge(sp_m, sp_l, sp_o, a->B * a->q * a->H, P, a->out, a->lse, s),
                   "decode_step: merge");
 }

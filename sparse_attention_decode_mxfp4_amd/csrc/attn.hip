@@ -37,6 +37,7 @@
 //   the dot product; PV folds the token scale into P.
 #include "common.hpp"
 #include "launch.hpp"
+#include "topk.hpp"
 
 namespace mxs {
 
@@ -96,178 +97,164 @@ __device__ __forceinline__ void load_block(BlockRegs<FMT> &r, const uint8_t *kp,
   }
 }
 
+// B operand of QK: head n's query as bf16, elements 32 kg + 8 s .. + 7 for
+// k-step s (the order of the key groups each lane loads). An e4m3 query is
+// widened exactly; a bf16 query is loaded as is. Heads >= H load head 0 and
+// are zeroed (unconditional loads).
 template <int FMT>
-__global__ __launch_bounds__(256) void k_split_attn(CacheView c, const void *__restrict__ qv,
-                                                    const int32_t *__restrict__ block_table,
-                                                    int32_t q_rows, int32_t H, int32_t topk, int32_t P,
-                                                    float sm_scale, float *__restrict__ sp_m,
-                                                    float *__restrict__ sp_l, float *__restrict__ sp_o) {
-  __shared__ float s_m[kAttnWaves][16], s_l[kAttnWaves][16];
-  __shared__ float s_o[kAttnWaves][16][kDim + 4];
-  const int p = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-  const int row = b * q_rows + j;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 15, kg = lane >> 4;
-  const int pos = c.context_lens[b] - q_rows + j;
-  const int cps = (topk + P - 1) / P;
-  const int slot0 = p * cps, slot1 = min(slot0 + cps, (int)topk);
-  const float NEG_INF = -__builtin_inff();
+__device__ __forceinline__ void load_query(const void *__restrict__ qv, int row, int H, int n, int kg, bf16x8 qbf[4]) {
+  const int hq = n < H ? n : 0;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    u32x4 v;
+    if constexpr (FMT == 0) {
+      const uint2 c8 = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint8_t *>(qv) +
+                                                        ((int64_t)row * H + hq) * kDim + 32 * kg + 8 * s);
+      const uint2 x = e4m3x4_to_bf16(c8.x), y = e4m3x4_to_bf16(c8.y);
+      v = u32x4{x.x, x.y, y.x, y.y};
+    } else {
+      v = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(qv) + ((int64_t)row * H + hq) * kDim +
+                                           32 * kg + 8 * s);
+    }
+    if (n >= H) v = u32x4{0u, 0u, 0u, 0u};
+    qbf[s] = __builtin_bit_cast(bf16x8, v);
+  }
+}
 
-  // B operand of QK: head n's query as bf16, elements 32 kg + 8 s .. + 7 for
-  // k-step s (the order of the key groups each lane loads). An e4m3 query is
-  // widened exactly; a bf16 query is loaded as is. Heads >= H load head 0 and
-  // are zeroed (unconditional loads).
-  bf16x8 qbf[4];
-  {
-    const int hq = n < H ? n : 0;
+// One selected block (page `phys`, first token position t0) folded into this
+// wave's online softmax state (m_run, l_run, O) for head n = lane % 16.
+template <int FMT>
+__device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t0, int pos, const bf16x8 qbf[4],
+                                             float sm_scale, float &m_run, float &l_run, f32x4 O[8], int n, int kg) {
+  const float NEG_INF = -__builtin_inff();
+  const int64_t pb = (int64_t)phys * (FMT == 0 ? kMxPageBytes : kF8PageBytes);
+  BlockRegs<FMT> r;
+  load_block<FMT>(r, c.k_pages + pb, c.v_pages + pb, n, kg);
+
+  // ---- QK: scores of tokens 16 nt + 4 kg + i for head n
+  float sc[8][4];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    const bool live = t0 + 16 * nt + n <= pos;       // the lane's A row (token 16 nt + n)
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      u32x4 v;
+      u32x4 a;
       if constexpr (FMT == 0) {
-        const uint2 c8 = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint8_t *>(qv) +
-                                                          ((int64_t)row * H + hq) * kDim + 32 * kg + 8 * s);
-        const uint2 x = e4m3x4_to_bf16(c8.x), y = e4m3x4_to_bf16(c8.y);
-        v = u32x4{x.x, x.y, y.x, y.y};
+        uint32_t w4[4];
+        fp4x8_to_bf16(live ? r.k[nt][s] : 0u, e8m0_f32(live ? r.ks[nt] : 127u), w4);
+        a = u32x4{w4[0], w4[1], w4[2], w4[3]};
       } else {
-        v = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(qv) +
-                                             ((int64_t)row * H + hq) * kDim + 32 * kg + 8 * s);
+        const u32x4 &src = r.k[nt][s >> 1];
+        const uint2 x = e4m3x4_to_bf16(live ? src[2 * (s & 1)] : 0u);
+        const uint2 y = e4m3x4_to_bf16(live ? src[2 * (s & 1) + 1] : 0u);
+        a = u32x4{x.x, x.y, y.x, y.y};
       }
-      if (n >= H) v = u32x4{0u, 0u, 0u, 0u};
-      qbf[s] = __builtin_bit_cast(bf16x8, v);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qbf[s], acc, 0, 0, 0);
     }
-  }
-
-  float m_run = NEG_INF, l_run = 0.0f;
-  f32x4 O[8];
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int slot = slot0 + wave; slot < slot1; slot += kAttnWaves) {
-    const int blk = block_table[(int64_t)row * topk + slot];
-    if (blk < 0 || blk >= c.stride || blk * kTokens > pos) continue;
-    const int phys = c.page_table[(int64_t)b * c.stride + blk];
-    if (phys < 0 || phys >= c.num_pages) continue;
-    const int t0 = blk * kTokens;            // position of the page's first token
-    const int64_t pb = (int64_t)phys * (FMT == 0 ? kMxPageBytes : kF8PageBytes);
-    BlockRegs<FMT> r;
-    load_block<FMT>(r, c.k_pages + pb, c.v_pages + pb, n, kg);
-
-    // ---- QK: scores of tokens 16 nt + 4 kg + i for head n
-    float sc[8][4];
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const bool live = t0 + 16 * nt + n <= pos;       // the lane's A row (token 16 nt + n)
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        u32x4 a;
-        if constexpr (FMT == 0) {
-          uint32_t w4[4];
-          fp4x8_to_bf16(live ? r.k[nt][s] : 0u, e8m0_f32(live ? r.ks[nt] : 127u), w4);
-          a = u32x4{w4[0], w4[1], w4[2], w4[3]};
-        } else {
-          const u32x4 &src = r.k[nt][s >> 1];
-          const uint2 x = e4m3x4_to_bf16(live ? src[2 * (s & 1)] : 0u);
-          const uint2 y = e4m3x4_to_bf16(live ? src[2 * (s & 1) + 1] : 0u);
-          a = u32x4{x.x, x.y, y.x, y.y};
-        }
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qbf[s], acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = acc[i] * sm_scale;
-        if constexpr (FMT == 1) x *= r.ks[nt][i];
-        sc[nt][i] = (t0 + 16 * nt + 4 * kg + i <= pos) ? x : NEG_INF;
-      }
-    }
-
-    // ---- online softmax for head n
-    float bm = NEG_INF;
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bm = fmaxf(bm, sc[nt][i]);
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float m_new = fmaxf(m_run, bm);
-    const float alpha = __expf(m_run - m_new);      // 0 when m_run is -inf
-    float ps = 0.f;
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sc[nt][i] = __expf(sc[nt][i] - m_new);      // masked tokens: exp(-inf) = 0
-        ps += sc[nt][i];
-      }
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-    // rescale O rows (heads 4 kg + i) by their head's alpha
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float ai = __shfl(alpha, 4 * kg + i);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) O[dt][i] *= ai;
-    }
-
-    // ---- PV over 4 k-steps of 32 tokens
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4 pa;                                     // P of the lane's 8 tokens as bf16
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        float p0 = sc[2 * s + (h >> 1)][2 * (h & 1)], p1 = sc[2 * s + (h >> 1)][2 * (h & 1) + 1];
-        if constexpr (FMT == 1) {
-          // fold V's token scale into P; masked tokens keep p = 0 (their scale may be NaN)
-          const f32x4 &vs = r.vs[s][h >> 1];
-          p0 = p0 == 0.0f ? 0.0f : p0 * vs[2 * (h & 1)];
-          p1 = p1 == 0.0f ? 0.0f : p1 * vs[2 * (h & 1) + 1];
-        }
-        pa[h] = bf16_bits_rne(p0) | (bf16_bits_rne(p1) << 16);
-      }
-      if constexpr (FMT == 0) {
-        uint32_t W[8][4];                           // token e, byte cb -> bf16 pair (d-tiles 2 cb, 2 cb + 1)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bool live = t0 + pv_token(s, kg, e) <= pos;
-          const uint32_t sb = (r.vs[s][e >> 2][e & 3] >> (8 * (n >> 2))) & 0xFFu;
-          fp4x8_to_bf16(live ? r.v[s][e] : 0u, e8m0_f32(live ? sb : 127u), W[e]);
-        }
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          const u32x4 blo = {lo_pair(W[0][cb], W[1][cb]), lo_pair(W[2][cb], W[3][cb]), lo_pair(W[4][cb], W[5][cb]),
-                             lo_pair(W[6][cb], W[7][cb])};
-          const u32x4 bhi = {hi_pair(W[0][cb], W[1][cb]), hi_pair(W[2][cb], W[3][cb]), hi_pair(W[4][cb], W[5][cb]),
-                             hi_pair(W[6][cb], W[7][cb])};
-          O[2 * cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
-                                                              __builtin_bit_cast(bf16x8, blo), O[2 * cb], 0, 0, 0);
-          O[2 * cb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
-                                                                  __builtin_bit_cast(bf16x8, bhi), O[2 * cb + 1], 0, 0, 0);
-        }
-      } else {
-        uint32_t X0[8], X1[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bool live = t0 + pv_token(s, kg, e) <= pos;
-          X0[e] = live ? r.v[s][e].x : 0u;
-          X1[e] = live ? r.v[s][e].y : 0u;
-        }
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          u32x4 bv;
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const uint32_t ca = ((dt < 4 ? X0[2 * h] : X1[2 * h]) >> (8 * (dt & 3))) & 0xFFu;
-            const uint32_t cb = ((dt < 4 ? X0[2 * h + 1] : X1[2 * h + 1]) >> (8 * (dt & 3))) & 0xFFu;
-            bv[h] = e4m3_bf16_bits(ca) | (e4m3_bf16_bits(cb) << 16);
-          }
-          O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
-                                                          __builtin_bit_cast(bf16x8, bv), O[dt], 0, 0, 0);
-        }
-      }
+      float x = acc[i] * sm_scale;
+      if constexpr (FMT == 1) x *= r.ks[nt][i];
+      sc[nt][i] = (t0 + 16 * nt + 4 * kg + i <= pos) ? x : NEG_INF;
     }
   }
 
-  // ---- this wave's sums for head n, then the 4-wave merge through LDS
+  // ---- online softmax for head n
+  float bm = NEG_INF;
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bm = fmaxf(bm, sc[nt][i]);
+  bm = fmaxf(bm, __shfl_xor(bm, 16));
+  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  const float m_new = fmaxf(m_run, bm);
+  const float alpha = __expf(m_run - m_new);      // 0 when m_run is -inf
+  float ps = 0.f;
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[nt][i] = __expf(sc[nt][i] - m_new);      // masked tokens: exp(-inf) = 0
+      ps += sc[nt][i];
+    }
+  l_run = l_run * alpha + ps;
+  m_run = m_new;
+  // rescale O rows (heads 4 kg + i) by their head's alpha
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float ai = __shfl(alpha, 4 * kg + i);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) O[dt][i] *= ai;
+  }
+
+  // ---- PV over 4 k-steps of 32 tokens
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    u32x4 pa;                                     // P of the lane's 8 tokens as bf16
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float p0 = sc[2 * s + (h >> 1)][2 * (h & 1)], p1 = sc[2 * s + (h >> 1)][2 * (h & 1) + 1];
+      if constexpr (FMT == 1) {
+        // fold V's token scale into P; masked tokens keep p = 0 (their scale may be NaN)
+        const f32x4 &vs = r.vs[s][h >> 1];
+        p0 = p0 == 0.0f ? 0.0f : p0 * vs[2 * (h & 1)];
+        p1 = p1 == 0.0f ? 0.0f : p1 * vs[2 * (h & 1) + 1];
+      }
+      pa[h] = bf16_bits_rne(p0) | (bf16_bits_rne(p1) << 16);
+    }
+    if constexpr (FMT == 0) {
+      uint32_t W[8][4];                           // token e, byte cb -> bf16 pair (d-tiles 2 cb, 2 cb + 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool live = t0 + pv_token(s, kg, e) <= pos;
+        const uint32_t sb = (r.vs[s][e >> 2][e & 3] >> (8 * (n >> 2))) & 0xFFu;
+        fp4x8_to_bf16(live ? r.v[s][e] : 0u, e8m0_f32(live ? sb : 127u), W[e]);
+      }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const u32x4 blo = {lo_pair(W[0][cb], W[1][cb]), lo_pair(W[2][cb], W[3][cb]), lo_pair(W[4][cb], W[5][cb]),
+                           lo_pair(W[6][cb], W[7][cb])};
+        const u32x4 bhi = {hi_pair(W[0][cb], W[1][cb]), hi_pair(W[2][cb], W[3][cb]), hi_pair(W[4][cb], W[5][cb]),
+                           hi_pair(W[6][cb], W[7][cb])};
+        O[2 * cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
+                                                            __builtin_bit_cast(bf16x8, blo), O[2 * cb], 0, 0, 0);
+        O[2 * cb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
+                                                                __builtin_bit_cast(bf16x8, bhi), O[2 * cb + 1], 0, 0, 0);
+      }
+    } else {
+      uint32_t X0[8], X1[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool live = t0 + pv_token(s, kg, e) <= pos;
+        X0[e] = live ? r.v[s][e].x : 0u;
+        X1[e] = live ? r.v[s][e].y : 0u;
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        u32x4 bv;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const uint32_t ca = ((dt < 4 ? X0[2 * h] : X1[2 * h]) >> (8 * (dt & 3))) & 0xFFu;
+          const uint32_t cb = ((dt < 4 ? X0[2 * h + 1] : X1[2 * h + 1]) >> (8 * (dt & 3))) & 0xFFu;
+          bv[h] = e4m3_bf16_bits(ca) | (e4m3_bf16_bits(cb) << 16);
+        }
+        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
+                                                        __builtin_bit_cast(bf16x8, bv), O[dt], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// This wave's sums for head n, then the 4-wave merge through LDS into the
+// workgroup's partial (m, l, O) of partition p.
+__device__ __forceinline__ void write_partial(float (&s_m)[kAttnWaves][16], float (&s_l)[kAttnWaves][16],
+                                              float (&s_o)[kAttnWaves][16][kDim + 4], float m_run, float l_run,
+                                              const f32x4 O[8], int row, int H, int P, int p, float *__restrict__ sp_m,
+                                              float *__restrict__ sp_l, float *__restrict__ sp_o) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, kg = lane >> 4;
+  const float NEG_INF = -__builtin_inff();
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   if (kg == 0) {
@@ -313,6 +300,97 @@ __global__ __launch_bounds__(256) void k_split_attn(CacheView c, const void *__r
   }
 }
 
+template <int FMT>
+__global__ __launch_bounds__(256) void k_split_attn(CacheView c, const void *__restrict__ qv,
+                                                    const int32_t *__restrict__ block_table,
+                                                    int32_t q_rows, int32_t H, int32_t topk, int32_t P,
+                                                    float sm_scale, float *__restrict__ sp_m,
+                                                    float *__restrict__ sp_l, float *__restrict__ sp_o) {
+  __shared__ float s_m[kAttnWaves][16], s_l[kAttnWaves][16];
+  __shared__ float s_o[kAttnWaves][16][kDim + 4];
+  const int p = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int row = b * q_rows + j;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, kg = lane >> 4;
+  const int pos = c.context_lens[b] - q_rows + j;
+  const int cps = (topk + P - 1) / P;
+  const int slot0 = p * cps, slot1 = min(slot0 + cps, (int)topk);
+  bf16x8 qbf[4];
+  load_query<FMT>(qv, row, H, n, kg, qbf);
+
+  float m_run = -__builtin_inff(), l_run = 0.0f;
+  f32x4 O[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int slot = slot0 + wave; slot < slot1; slot += kAttnWaves) {
+    const int blk = block_table[(int64_t)row * topk + slot];
+    if (blk < 0 || blk >= c.stride || blk * kTokens > pos) continue;
+    const int phys = c.page_table[(int64_t)b * c.stride + blk];
+    if (phys < 0 || phys >= c.num_pages) continue;
+    attend_block<FMT>(c, phys, blk * kTokens, pos, qbf, sm_scale, m_run, l_run, O, n, kg);
+  }
+  write_partial(s_m, s_l, s_o, m_run, l_run, O, row, H, P, p, sp_m, sp_l, sp_o);
+}
+
+// The decode step's attention: the workgroup first selects its row's top-k
+// blocks itself (the workgroup selection of topk.hpp over the row's scores),
+// with the row's page table staged in LDS, then attends to the slots of its
+// partition. Everything it needs from memory before the K / V pages — the
+// context length, the score row, the page-table row and the query — is
+// requested in one round trip. Partition 0 also writes the row's block table.
+template <int FMT, int ITEMS>
+__global__ __launch_bounds__(256) void k_select_attn(CacheView c, const float *__restrict__ scores,
+                                                     const void *__restrict__ qv, int32_t q_rows, int32_t H,
+                                                     int32_t topk, int32_t P, float sm_scale,
+                                                     int32_t *__restrict__ block_table, float *__restrict__ sp_m,
+                                                     float *__restrict__ sp_l, float *__restrict__ sp_o) {
+  __shared__ TopkSmem<ITEMS> tk;
+  __shared__ int32_t s_pt[kTopkThreads * ITEMS];
+  __shared__ float s_m[kAttnWaves][16], s_l[kAttnWaves][16];
+  __shared__ float s_o[kAttnWaves][16][kDim + 4];
+  const int p = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int row = b * q_rows + j;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, kg = lane >> 4;
+  const int stride = c.stride;
+
+  const int L = c.context_lens[b];
+  float v[ITEMS];
+  int32_t pt[ITEMS];
+#pragma unroll
+  for (int r = 0; r < ITEMS; ++r) {
+    const int i = min(tid + kTopkThreads * r, stride - 1);   // clamped: unconditional loads
+    v[r] = scores[(int64_t)row * stride + i];
+    pt[r] = c.page_table[(int64_t)b * stride + i];
+  }
+  bf16x8 qbf[4];
+  load_query<FMT>(qv, row, H, n, kg, qbf);
+
+  const int pos = L - q_rows + j;
+  const int n_cand = pos < 0 ? 0 : min(pos / kTokens + 1, stride);
+#pragma unroll
+  for (int r = 0; r < ITEMS; ++r)
+    if (tid + kTopkThreads * r < stride) s_pt[tid + kTopkThreads * r] = pt[r];
+  int n_sel;
+  const uint32_t sel = wg_topk<ITEMS>(v, n_cand, topk, tk, n_sel);
+  __syncthreads();                                 // s_pt (the selection may return before any barrier)
+  if (p == 0 && tid < topk) block_table[(int64_t)row * topk + tid] = tid < n_sel ? (int32_t)sel : -1;
+
+  const int cps = (topk + P - 1) / P;
+  const int slot0 = p * cps, slot1 = min(slot0 + cps, n_sel);
+  float m_run = -__builtin_inff(), l_run = 0.0f;
+  f32x4 O[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int slot = slot0 + wave; slot < slot1; slot += kAttnWaves) {
+    const int blk = __builtin_amdgcn_readlane((int)sel, slot);      // a candidate: blk * 128 <= pos
+    const int phys = s_pt[blk];
+    if (phys < 0 || phys >= c.num_pages) continue;
+    attend_block<FMT>(c, phys, blk * kTokens, pos, qbf, sm_scale, m_run, l_run, O, n, kg);
+  }
+  write_partial(s_m, s_l, s_o, m_run, l_run, O, row, H, P, p, sp_m, sp_l, sp_o);
+}
+
 hipError_t launch_split_attn(const CacheView &c, const void *q, int q_dtype, const int32_t *block_table,
                              int32_t B, int32_t q_rows, int32_t H, int32_t topk, int32_t P, float sm_scale,
                              float *sp_m, float *sp_l, float *sp_o, hipStream_t s) {
@@ -325,6 +403,27 @@ hipError_t launch_split_attn(const CacheView &c, const void *q, int q_dtype, con
   else
     hipLaunchKernelGGL(k_split_attn<1>, grid, dim3(256), 0, s, c, q, block_table, q_rows, H, topk, P, sm_scale,
                        sp_m, sp_l, sp_o);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_attn(const CacheView &c, const float *scores, const void *q, int32_t B, int32_t q_rows,
+                              int32_t H, int32_t topk, int32_t P, float sm_scale, int32_t *block_table, float *sp_m,
+                              float *sp_l, float *sp_o, hipStream_t s) {
+  if (B * q_rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)P, (unsigned)q_rows, (unsigned)B), block(kTopkThreads);
+#define MXS_SELECT_ATTN(F, I)                                                                                   \
+  hipLaunchKernelGGL((k_select_attn<F, I>), grid, block, 0, s, c, scores, q, q_rows, H, topk, P, sm_scale,     \
+                     block_table, sp_m, sp_l, sp_o)
+  if (c.kv_format == 0) {
+    if (c.stride <= kTopkThreads * 2) MXS_SELECT_ATTN(0, 2);
+    else if (c.stride <= kTopkThreads * 8) MXS_SELECT_ATTN(0, 8);
+    else MXS_SELECT_ATTN(0, 32);
+  } else {
+    if (c.stride <= kTopkThreads * 2) MXS_SELECT_ATTN(1, 2);
+    else if (c.stride <= kTopkThreads * 8) MXS_SELECT_ATTN(1, 8);
+    else MXS_SELECT_ATTN(1, 32);
+  }
+#undef MXS_SELECT_ATTN
   return hipGetLastError();
 }
 

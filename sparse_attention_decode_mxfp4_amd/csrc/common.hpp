@@ -111,6 +111,46 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t d) {
 }
 
 // ---------------------------------------------------------------- wave helpers
+// The value lane (lane ^ M) holds, for M a power of two below 64:
+//   1, 2: DPP quad permutes; 8: row rotate by 8; 4: row rotates by 4 and 12
+//   (lane - 4 for lanes with bit 2 set, lane + 4 otherwise); 16, 32: the
+//   gfx950 permlane swaps of a value with itself, which hand each half its
+//   partner's copy.
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  const uint32_t lane = threadIdx.x & 63u;
+  if constexpr (M == 1) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+  } else if constexpr (M == 4) {
+    const uint32_t dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false);   // row_ror:4
+    const uint32_t up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x12C, 0xF, 0xF, false);   // row_ror:12
+    return (lane & 4u) ? dn : up;
+  } else if constexpr (M == 8) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);   // row_ror:8
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16u) ? r[0] : r[1];
+  } else {
+    static_assert(M == 32, "lane xor mask");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane & 32u) ? r[0] : r[1];
+  }
+}
+
+// xor_lane for a mask that is a constant once the caller's loop is unrolled
+__device__ __forceinline__ uint32_t xor_lane_n(uint32_t v, int m) {
+  switch (m) {
+    case 1: return xor_lane<1>(v);
+    case 2: return xor_lane<2>(v);
+    case 4: return xor_lane<4>(v);
+    case 8: return xor_lane<8>(v);
+    case 16: return xor_lane<16>(v);
+    default: return xor_lane<32>(v);
+  }
+}
+
 __device__ __forceinline__ float wave_max16(float v) {      // max over the 16 lanes sharing lane / 16
   v = fmaxf(v, __shfl_xor(v, 1));
   v = fmaxf(v, __shfl_xor(v, 2));

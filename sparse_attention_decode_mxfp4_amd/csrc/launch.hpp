@@ -44,6 +44,13 @@ hipError_t launch_split_attn(const CacheView &c, const void *q, int q_dtype,
                              int32_t topk, int32_t P, float sm_scale, float *sp_m, float *sp_l,
                              float *sp_o, hipStream_t s);
 
+// the decode step's attention (attn.hip): each workgroup selects its row's
+// top-k blocks from the scores [B][q_rows][stride] itself, writes the row's
+// block table (partition 0) and attends to its partition's slots
+hipError_t launch_select_attn(const CacheView &c, const float *scores, const void *q, int32_t B, int32_t q_rows,
+                              int32_t H, int32_t topk, int32_t P, float sm_scale, int32_t *block_table, float *sp_m,
+                              float *sp_l, float *sp_o, hipStream_t s);
+
 // merge (merge.hip)
 hipError_t launch_lse_merge(const float *sp_m, const float *sp_l, const float *sp_o, int32_t n_rows,
                             int32_t P, uint16_t *out, float *lse, hipStream_t s);

@@ -16,37 +16,62 @@
 
 namespace mxs {
 
-// Quantize one fp32 row (this wave's lane owns x = elements 2l, 2l+1) into
-// token `tok` of the MXFP4 page at `page`.
-__device__ __forceinline__ void mx_store_row(float2 x, uint8_t *page, int tok, int lane) {
+// Quantize one fp32 row, this wave's lane owning x = elements 2l, 2l+1: the
+// lane's code byte (low nibble element 2l) and the e8m0 scale byte of its
+// 32-element group (lanes 16 g .. 16 g + 15 hold group g).
+__device__ __forceinline__ void mx_quant_row(float2 x, uint32_t &code, uint32_t &sb) {
   uint32_t a = max(f2u(x.x) & 0x7FFFFFFFu, f2u(x.y) & 0x7FFFFFFFu);   // |.| bits order like values
-  a = max(a, (uint32_t)__shfl_xor((int)a, 1));
-  a = max(a, (uint32_t)__shfl_xor((int)a, 2));
-  a = max(a, (uint32_t)__shfl_xor((int)a, 4));
-  a = max(a, (uint32_t)__shfl_xor((int)a, 8));
-  const uint32_t sb = mx_scale_byte(a);
+  a = max(a, xor_lane<1>(a));                                          // the 16-lane group's max
+  a = max(a, xor_lane<2>(a));
+  a = max(a, xor_lane<4>(a));
+  a = max(a, xor_lane<8>(a));
+  sb = mx_scale_byte(a);
   const float inv = mx_inv_scale(sb);
-  const uint32_t c0 = e2m1_code(x.x * inv);
-  const uint32_t c1 = e2m1_code(x.y * inv);
-  page[64 * tok + lane] = (uint8_t)(c0 | (c1 << 4));
-  const uint32_t s1 = (uint32_t)__shfl((int)sb, 16);
-  const uint32_t s2 = (uint32_t)__shfl((int)sb, 32);
-  const uint32_t s3 = (uint32_t)__shfl((int)sb, 48);
+  code = e2m1_code(x.x * inv) | (e2m1_code(x.y * inv) << 4);
+}
+
+// The four group scale bytes of a quantized row as the page's scale dword
+// (group g's byte from lane 16 g), the same in every lane.
+__device__ __forceinline__ uint32_t mx_scale_word(uint32_t sb) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)sb, 0) | ((uint32_t)__builtin_amdgcn_readlane((int)sb, 16) << 8) |
+         ((uint32_t)__builtin_amdgcn_readlane((int)sb, 32) << 16) |
+         ((uint32_t)__builtin_amdgcn_readlane((int)sb, 48) << 24);
+}
+
+// The quantized row into token `tok` of the MXFP4 page at `page`.
+__device__ __forceinline__ void mx_write_row(uint32_t code, uint32_t sb, uint8_t *page, int tok, int lane) {
+  page[64 * tok + lane] = (uint8_t)code;
   if (lane == 0)
-    *reinterpret_cast<uint32_t *>(page + kMxScaleOff + 4 * tok) = sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
+    *reinterpret_cast<uint32_t *>(page + kMxScaleOff + 4 * tok) = mx_scale_word(sb);
+}
+
+__device__ __forceinline__ void mx_store_row(float2 x, uint8_t *page, int tok, int lane) {
+  uint32_t code, sb;
+  mx_quant_row(x, code, sb);
+  mx_write_row(code, sb, page, tok, lane);
 }
 
 // FP8 per-token row: scale = fp32(amax / 448) (1 for an all-zero row),
-// code = e4m3(fp32(x / scale)); IEEE division on both.
-__device__ __forceinline__ void f8_store_row(float2 x, uint8_t *page, int tok, int lane) {
+// code = e4m3(fp32(x / scale)); IEEE division on both. codes: the lane's two
+// code bytes (element 2l in the low byte).
+__device__ __forceinline__ void f8_quant_row(float2 x, uint32_t &codes, float &scale) {
   uint32_t a = max(f2u(x.x) & 0x7FFFFFFFu, f2u(x.y) & 0x7FFFFFFFu);
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) a = max(a, (uint32_t)__shfl_xor((int)a, o));
+  a = max(a, xor_lane<1>(a));                                          // the row's max
+  a = max(a, xor_lane<2>(a));
+  a = max(a, xor_lane<4>(a));
+  a = max(a, xor_lane<8>(a));
+  a = max(a, xor_lane<16>(a));
+  a = max(a, xor_lane<32>(a));
   const float amax = u2f(a);
-  const float scale = amax == 0.0f ? 1.0f : amax / 448.0f;
-  const uint32_t c0 = e4m3_code(x.x / scale);
-  const uint32_t c1 = e4m3_code(x.y / scale);
-  *reinterpret_cast<uint16_t *>(page + 128 * tok + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
+  scale = amax == 0.0f ? 1.0f : amax / 448.0f;
+  codes = e4m3_code(x.x / scale) | (e4m3_code(x.y / scale) << 8);
+}
+
+__device__ __forceinline__ void f8_store_row(float2 x, uint8_t *page, int tok, int lane) {
+  uint32_t codes;
+  float scale;
+  f8_quant_row(x, codes, scale);
+  *reinterpret_cast<uint16_t *>(page + 128 * tok + 2 * lane) = (uint16_t)codes;
   if (lane == 0) *reinterpret_cast<float *>(page + kF8ScaleOff + 4 * tok) = scale;
 }
 

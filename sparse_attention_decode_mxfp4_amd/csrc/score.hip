@@ -46,12 +46,15 @@ template <int FMT> struct Chunk;
 template <> struct Chunk<0> { static constexpr int kCodes = 4096, kBytes = 4096 + 256, kDma = 5, kPage = kMxPageBytes, kScale = kMxScaleOff; };
 template <> struct Chunk<1> { static constexpr int kCodes = 8192, kBytes = 8192 + 256, kDma = 9, kPage = kF8PageBytes, kScale = kF8ScaleOff; };
 
-// Launch shape per index format: waves per workgroup, pages per wave, LDS
-// stages per wave. MXFP4: 4 x 4 x 4 stages of 4.25 KiB = 68 KiB of LDS per
-// workgroup, two workgroups per CU, ~100 KiB of copies in flight per CU.
-template <int FMT> struct ScoreShape;
-template <> struct ScoreShape<0> { static constexpr int kWaves = 4, kPages = 4, kStages = 4; };
-template <> struct ScoreShape<1> { static constexpr int kWaves = 4, kPages = 2, kStages = 2; };
+// Launch shapes: waves per workgroup, pages per wave, LDS stages per wave.
+// Measured on MI355X (MXFP4 index, 4 sequences): 4 x 8 x 3 is fastest once
+// the grid still gives every CU a workgroup (256 workgroups at 2048 pages per
+// sequence: 16.9 us against 17.6 us for 4 x 4 x 2 and 18.3 us for 4 x 2 x 2);
+// smaller page tables want more, shorter workgroups (512 pages: 4 x 1 x 2 at
+// 6.9 us against 7.1 us for 4 x 2 x 2 and 9.6 us for 4 x 4 x 2).
+template <int NW_, int PPW_, int S_> struct Shape {
+  static constexpr int kWaves = NW_, kPages = PPW_, kStages = S_;
+};
 
 // s_waitcnt vmcnt(n * D) for a wave-uniform n <= K that is a constant once the
 // chunk loop is unrolled: at most the n most recently issued chunks (D copies
@@ -135,33 +138,115 @@ __device__ __forceinline__ void key_operands(const uint8_t *stage, int nt, int n
   }
 }
 
-// The decode step's K / V row stores and q pack for sequence b, spread over
-// the sequence's NW-wave workgroups (nothing in this launch reads them; the
-// attention launch that follows does): row r of the 2q K / V rows goes to wave
-// r of the sequence's waves, q element 4i to thread i.
-template <int NW>
-__device__ __forceinline__ void step_side_stores(const CacheView &c, const StepStore &st, int b, int q, int L,
-                                                 int lane, int wave) {
-  const int nwg = gridDim.x;
-  if (st.k_new) {
-    for (int r = blockIdx.x * NW + wave; r < 2 * q; r += nwg * NW) {
-      const int j = r % q, t = L - q + j;
-      if (t < 0 || t / kTokens >= c.stride) continue;
-      const int page = c.page_table[(int64_t)b * c.stride + t / kTokens];
-      if (page < 0 || page >= c.num_pages) continue;
-      const float *src = (r < q ? st.k_new : st.v_new) + ((int64_t)b * q + j) * kDim;
-      uint8_t *pool = r < q ? c.k_pages : c.v_pages;
-      const float2 x = reinterpret_cast<const float2 *>(src)[lane];
-      if (c.kv_format == 0)
-        mx_store_row(x, pool + (int64_t)page * kMxPageBytes, t % kTokens, lane);
-      else
-        f8_store_row(x, pool + (int64_t)page * kF8PageBytes, t % kTokens, lane);
-    }
+// The decode step's new K / V / index rows and e4m3 query, spread over the
+// sequence's scoring waves: wave gw (of n_waves) stores rows r = gw + k
+// n_waves of the 3q new rows (r < q: K row r; < 2q: V row r - q; else index
+// row r - 2q; row j goes to position L - q + j) and packs query elements
+// 64 (gw + k n_waves) + lane. The first round's sources are requested in the
+// scorer's prologue and stored after the wave's last chunk, so the copies
+// never wait for them; later rounds (page tables too short to give every row
+// a wave) load and store at the end. Nothing in this launch reads the K / V
+// rows or the query; the index rows are scored from the wave that holds
+// their positions (see the kernel).
+struct SideWork {
+  float2 row = make_float2(0.f, 0.f);  // row gw, this lane's two elements
+  int page = -1;                       // its page (-1: none)
+  float qe = 0.f;                      // query element 64 gw + lane
+};
+
+__device__ __forceinline__ int side_rows(const StepStore &st, int q) {
+  return (st.k_new ? 2 * q : 0) + (st.idx_new ? q : 0);
+}
+
+// row r's source (K, V and index rows are numbered on when present)
+__device__ __forceinline__ const float *side_src(const StepStore &st, int b, int q, int r) {
+  const float *base = st.k_new ? (r < q ? st.k_new : (r < 2 * q ? st.v_new : st.idx_new)) : st.idx_new;
+  return base + ((int64_t)b * q + r % q) * kDim;
+}
+
+__device__ __forceinline__ int side_page(const CacheView &c, int b, int q, int L, int r) {
+  const int t = L - q + r % q;
+  if (t < 0 || t / kTokens >= c.stride) return -1;
+  return c.page_table[(int64_t)b * c.stride + t / kTokens];
+}
+
+__device__ __forceinline__ void side_row(const CacheView &c, const StepStore &st, int b, int q, int L, int r,
+                                         float2 x, int page, int lane) {
+  const int t = L - q + r % q;
+  if (page < 0 || page >= c.num_pages) return;
+  const bool kv = st.k_new && r < 2 * q;
+  uint8_t *pool = kv ? (r < q ? c.k_pages : c.v_pages) : c.idx_pages;
+  if ((kv ? c.kv_format : c.idx_format) == 0)
+    mx_store_row(x, pool + (int64_t)page * kMxPageBytes, t % kTokens, lane);
+  else
+    f8_store_row(x, pool + (int64_t)page * kF8PageBytes, t % kTokens, lane);
+}
+
+// first-round sources (no dependence on the context length)
+__device__ __forceinline__ void side_prefetch(const StepStore &st, int b, int q, int gw, int lane, SideWork &sw) {
+  if (gw < side_rows(st, q)) sw.row = reinterpret_cast<const float2 *>(side_src(st, b, q, gw))[lane];
+  if (st.q8) {
+    const int64_t n = (int64_t)q * st.H * kDim, i = 64 * (int64_t)gw + lane;
+    if (i < n) sw.qe = load_q_elem(st.q_att, st.q_dtype, (int64_t)b * n + i);
   }
+}
+
+__device__ __forceinline__ void side_finish(const CacheView &c, const StepStore &st, int b, int q, int L, int gw,
+                                            int n_waves, int lane, const SideWork &sw) {
+  const int nr = side_rows(st, q);
+  if (gw < nr) side_row(c, st, b, q, L, gw, sw.row, sw.page, lane);
+  for (int r = gw + n_waves; r < nr; r += n_waves)
+    side_row(c, st, b, q, L, r, reinterpret_cast<const float2 *>(side_src(st, b, q, r))[lane],
+             side_page(c, b, q, L, r), lane);
   if (st.q8) {
     const int64_t n = (int64_t)q * st.H * kDim, base = (int64_t)b * n;
-    for (int64_t i = 4 * ((int64_t)blockIdx.x * 64 * NW + threadIdx.x); i < n; i += 4 * (int64_t)nwg * 64 * NW)
-      pack_q4(st.q_att, st.q_dtype, base + n, st.q8, base + i);
+    int64_t i = 64 * (int64_t)gw + lane;
+    if (i < n) st.q8[base + i] = (uint8_t)e4m3_code(sw.qe);
+    for (i += 64 * (int64_t)n_waves; i < n; i += 64 * (int64_t)n_waves)
+      st.q8[base + i] = (uint8_t)e4m3_code(load_q_elem(st.q_att, st.q_dtype, base + i));
+  }
+}
+
+// A new row quantized by one wave (this lane: elements 2 lane, 2 lane + 1):
+// code = the lane's code byte (MXFP4) or byte pair (FP8); gsb = the e8m0 byte
+// of the lane's 32-element group (MXFP4); word = the token's scale dword as
+// the page holds it (MXFP4: the four group bytes; FP8: the fp32 scale bits).
+template <int FMT>
+__device__ __forceinline__ void quant_row(float2 x, uint32_t &code, uint32_t &gsb, uint32_t &word) {
+  if constexpr (FMT == 0) {
+    mx_quant_row(x, code, gsb);
+    word = mx_scale_word(gsb);
+  } else {
+    float scale;
+    f8_quant_row(x, code, scale);
+    gsb = 0u;
+    word = f2u(scale);
+  }
+}
+
+// The quantized row into token tc of a chunk held in LDS in the copy layout
+// (see the chunk staging above). Called only once the chunk's copy has
+// landed (the explicit wait before it): the LDS writes are issued as plain
+// instructions, which the compiler would otherwise hold back behind every
+// copy still in flight; a wave's LDS operations execute in order, so the
+// chunk's reads that follow see them.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
+  return (uint32_t)(uintptr_t)(lds_ptr_t)const_cast<uint8_t *>(p);
+}
+template <int FMT>
+__device__ __forceinline__ void patch_row(uint8_t *stage, int tc, uint32_t code, uint32_t word, int lane) {
+  const int nt = tc >> 4, nn = tc & 15;
+  if constexpr (FMT == 0) {
+    asm volatile("ds_write_b8 %0, %1" ::"v"(lds_addr(stage + 1024 * nt + 256 * (lane >> 4) + 16 * nn + (lane & 15))),
+                 "v"(code) : "memory");
+    if (lane == 0)
+      asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(stage + Chunk<0>::kCodes + 4 * tc)), "v"(word) : "memory");
+  } else {
+    asm volatile("ds_write_b16 %0, %1" ::"v"(lds_addr(stage + 1024 * (2 * nt + ((lane & 15) >> 3)) +
+                                                        16 * (16 * (lane >> 4) + nn) + 2 * (lane & 7))),
+                 "v"(code) : "memory");
+    if (lane == 0)
+      asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(stage + Chunk<1>::kCodes + 4 * tc)), "v"(word) : "memory");
   }
 }
 
@@ -170,25 +255,36 @@ __global__ __launch_bounds__(64 * NW) void k_index_score(CacheView c, const uint
                                                          const float *__restrict__ w, int32_t q, int32_t H_I,
                                                          float *__restrict__ scores, StepStore st) {
   using CK = Chunk<FMT>;
-  __shared__ __attribute__((aligned(16))) uint8_t stages[NW][S][CK::kBytes];
-  const int b = blockIdx.y;
+  constexpr int kUnits = 2 * PPW;
+  static_assert(S >= 2 && S - 1 <= kUnits, "stage ring");
+  // One LDS object (a second one makes the compiler wait for every copy in
+  // flight before any LDS read): the wave's stages, then the step's new index
+  // rows quantized (4 MT rows: 64 lane words, then one scale word each).
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NW * S * CK::kBytes + 4 * MT * 65 * 4];
+  auto stage_at = [&](int w, int u) { return lds + (w * S + u) * CK::kBytes; };
+  uint32_t *s_qc = reinterpret_cast<uint32_t *>(lds + NW * S * CK::kBytes);   // [4 MT][64]
+  uint32_t *s_qw = s_qc + 4 * MT * 64;                                        // [4 MT]
+  // grid (sequence, wave group). Waves are numbered in dispatch order, d, and
+  // take the sequence's pages from the back (d = 0: the last pages, where the
+  // step's new rows are, so the wave with the most extra work starts first);
+  // the side stores go to the next waves dispatched.
+  const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, kg = lane >> 4;
-  const int p0 = (blockIdx.x * NW + wave) * PPW;
+  const int n_waves = gridDim.y * NW, d = blockIdx.y * NW + wave;
+  const int gw = (d + n_waves - 1) % n_waves;        // side-store index: d = 1, 2, ... first
+  const int p0 = (n_waves - 1 - d) * PPW;
   const float NEG_INF = -__builtin_inff();
   float *srow = scores + (int64_t)b * q * c.stride;
-  if (p0 >= c.stride) {                             // the grid's rounding: no pages
-    step_side_stores<NW>(c, st, b, q, c.context_lens[b], lane, wave);
-    return;
-  }
 
   // ---- prologue, one round trip: the context length, this wave's page ids
   // (clamped to the table row, so every load is unconditional; entries past
-  // the context or out of range are masked below), the A operand and weights.
+  // the context or out of range are masked below), the A operand, the weights
+  // and the wave's share of the step's side stores.
+  static_assert((PPW & (PPW - 1)) == 0 && PPW <= 64, "pages per wave: a power of two");
   const int L = c.context_lens[b];
-  int raw[PPW];
-#pragma unroll
-  for (int i = 0; i < PPW; ++i) raw[i] = c.page_table[(int64_t)b * c.stride + min(p0 + i, c.stride - 1)];
+  const int pk = lane & (PPW - 1);                   // lane k holds page p0 + k's id
+  const int praw = c.page_table[(int64_t)b * c.stride + min(p0 + pk, c.stride - 1)];
 
   // A operand: q_idx rows m = 16 mt + n -> (query row m / 4, head m % 4); rows
   // past q or H_I are zero (their load reads row 0 and is discarded)
@@ -217,6 +313,15 @@ __global__ __launch_bounds__(64 * NW) void k_index_score(CacheView c, const uint
       wv[mt][i] = ok ? x : 0.0f;
     }
   }
+  SideWork sw;
+  side_prefetch(st, b, q, gw, lane, sw);
+  // the step's new index rows, requested by every wave (16 KiB per sequence,
+  // L2-resident); only the wave that holds their positions keeps them
+  float2 xr[4 * MT];
+#pragma unroll
+  for (int j = 0; j < 4 * MT; ++j)
+    xr[j] = st.idx_new ? reinterpret_cast<const float2 *>(st.idx_new + ((int64_t)b * q + min(j, q - 1)) * kDim)[lane]
+                       : make_float2(0.f, 0.f);
   // Consume every prologue load here, so that no compiler-placed wait for them
   // lands inside the chunk pipeline (the compiler does not count the
   // direct-to-LDS copies and would wait for all of them).
@@ -227,126 +332,165 @@ __global__ __launch_bounds__(64 * NW) void k_index_score(CacheView c, const uint
 #pragma unroll
     for (int s = 0; s < 4; ++s) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, A[mt][s])));
   }
+  asm volatile("" ::"v"(praw));
+  asm volatile("" ::"v"(sw.row.x), "v"(sw.row.y), "v"(sw.qe));
 #pragma unroll
-  for (int i = 0; i < PPW; ++i) asm volatile("" ::"v"(raw[i]));
+  for (int j = 0; j < 4 * MT; ++j) asm volatile("" ::"v"(xr[j].x), "v"(xr[j].y));
   asm volatile("" ::"s"(L) : "memory");
 
   const int lim = min((L + kTokens - 1) / kTokens, (int)c.stride);    // pages holding tokens
-  if (p0 >= lim) {                                  // past the context: no candidates here
-    for (int i = 0; i < PPW && p0 + i < c.stride; ++i)
-      if (n == 0)
+  // The step's new index rows are quantized by the waves of the workgroup
+  // that holds their positions (rows j = wave, wave + NW, ... each, into LDS;
+  // every wave of it, on either path below, so the barrier sees all of them).
+  const int wg_p0 = (n_waves - NW * (blockIdx.y + 1)) * PPW;          // the workgroup's first page
+  const bool own_wg = st.idx_new != nullptr && L >= 1 && L - 1 >= wg_p0 * kTokens &&
+                      max(L - q, 0) < (wg_p0 + NW * PPW) * kTokens;     // uniform over the workgroup
+  auto quant_share = [&]() {
+    if (!own_wg) return;
+#pragma unroll
+    for (int j = 0; j < 4 * MT; ++j) {
+      if (j % NW != wave) continue;
+      uint32_t code, gsb, word;
+      quant_row<FMT>(xr[j], code, gsb, word);
+      s_qc[64 * j + lane] = code;
+      if (lane == 0) s_qw[j] = word;
+    }
+    // LDS writes done, then the workgroup barrier (no wait for the copies)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  if (gw < side_rows(st, q)) sw.page = side_page(c, b, q, L, gw);
+  if (p0 >= lim) {                                  // past the context (or the table): no candidates here
+    quant_share();
+    if (n == 0)
+      for (int i = 0; i < PPW && p0 + i < c.stride; ++i)
         for (int jw = kg; jw < q; jw += 4) srow[(int64_t)jw * c.stride + p0 + i] = NEG_INF;
-    step_side_stores<NW>(c, st, b, q, L, lane, wave);
-    return;
-  }
-  int phys[PPW];
-  bool valid[PPW];
+  } else {
+    // page p0 + i: valid (inside the context, id in range) = bit i of vmask,
+    // its id = lane i's praw (uniform reads, so no per-page registers)
+    const uint64_t vmask = __ballot(p0 + pk < lim && praw >= 0 && praw < c.num_pages);
+    auto valid_of = [&](int i) { return ((vmask >> i) & 1ull) != 0ull; };
+    auto phys_of = [&](int i) { return valid_of(i) ? __builtin_amdgcn_readlane(praw, i) : 0; };
+    int posw[MT];
 #pragma unroll
-  for (int i = 0; i < PPW; ++i) {
-    valid[i] = p0 + i < lim && raw[i] >= 0 && raw[i] < c.num_pages;
-    phys[i] = valid[i] ? raw[i] : 0;
-  }
-  int posw[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) posw[mt] = L - q + 4 * mt + kg;
-  const int pos_min = L - q;                        // the first query row's position
+    for (int mt = 0; mt < MT; ++mt) posw[mt] = L - q + 4 * mt + kg;
+    const int pos_min = L - q;                        // the first query row's position
 
-  // The step's new index rows that fall in this wave's pages are stored here,
-  // before the pages are copied; the wave waits for its own stores, which
-  // reach L2 before the copies read it (nothing cached them earlier).
-  if (st.idx_new && L - 1 >= p0 * kTokens && L - q < (p0 + PPW) * kTokens) {
-#pragma unroll
-    for (int i = 0; i < PPW; ++i) {
-      if (!valid[i]) continue;
-      for (int j = 0; j < q; ++j) {
-        const int t = L - q + j;
-        if (t < 0 || t / kTokens != p0 + i) continue;
-        const float2 x = reinterpret_cast<const float2 *>(st.idx_new + ((int64_t)b * q + j) * kDim)[lane];
-        if constexpr (FMT == 0)
-          mx_store_row(x, c.idx_pages + (int64_t)phys[i] * kMxPageBytes, t % kTokens, lane);
-        else
-          f8_store_row(x, c.idx_pages + (int64_t)phys[i] * kF8PageBytes, t % kTokens, lane);
-      }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-
-  // ---- the chunk pipeline. The waits are explicit (the compiler does not
-  // order LDS reads after direct-to-LDS loads): vmcnt counts this wave's
-  // vector memory operations in issue order, so "at most n chunks' copies
-  // outstanding" right after issuing chunk u + n means every older operation
-  // — chunk u's copies included — is done (younger stores only make the wait
-  // longer). Stage (u + S - 1) % S is refilled only after chunk u - 1, which
-  // it held, has been computed.
-  constexpr int kUnits = 2 * PPW;
-#pragma unroll
-  for (int u = 0; u < S - 1 && u < kUnits; ++u)
-    dma_chunk<FMT>(stages[wave][u], c.idx_pages + (int64_t)phys[u >> 1] * CK::kPage, u & 1, n, kg, lane);
-  // the side stores go out while the first copies are in flight
-  step_side_stores<NW>(c, st, b, q, L, lane, wave);
-
-  float rmax[MT];
-#pragma unroll
-  for (int u = 0; u < kUnits; ++u) {
-    const int i = u >> 1, h = u & 1;
-    const int p = p0 + i;
-    const uint8_t *stage = stages[wave][u % S];
-    if (u + S - 1 < kUnits) {
-      const int un = u + S - 1;
-      dma_chunk<FMT>(stages[wave][un % S], c.idx_pages + (int64_t)phys[un >> 1] * CK::kPage, un & 1, n, kg, lane);
-    }
-    wait_chunks<CK::kDma, S - 1>(min(S - 1, kUnits - 1 - u));
-    if (h == 0) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) rmax[mt] = NEG_INF;
-    }
-    // tokens of this chunk all at or before every row's position: no mask
-    const bool full = p * kTokens + 64 * h + 63 <= pos_min;
+    // rmax[mt] = max(rmax[mt], the row's score of every token t of chunk (p, h)
+    // with t_lo <= t <= hi[mt]) (all tokens when full)
+    auto chunk_max = [&](const uint8_t *stage, int p, int h, bool full, int t_lo, const int (&hi)[MT],
+                         float (&rmax)[MT]) {
 #pragma unroll 2
-    for (int nt = 0; nt < 4; ++nt) {
-      bf16x8 Bk[4];
-      float ksc;
-      key_operands<FMT>(stage, nt, n, kg, lane, Bk, ksc);
-      const int t = p * kTokens + 64 * h + 16 * nt + n;
+      for (int nt = 0; nt < 4; ++nt) {
+        bf16x8 Bk[4];
+        float ksc;
+        key_operands<FMT>(stage, nt, n, kg, lane, Bk, ksc);
+        const int t = p * kTokens + 64 * h + 16 * nt + n;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < MT; ++mt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][s], Bk[s], acc, 0, 0, 0);
-        float v = 0.f;
+          for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][s], Bk[s], acc, 0, 0, 0);
+          float v = 0.f;
 #pragma unroll
-        for (int hd = 0; hd < 4; ++hd) v += wv[mt][hd] * relu1(FMT == 1 ? acc[hd] * ksc : acc[hd]);
-        rmax[mt] = fmaxf(rmax[mt], (full || t <= posw[mt]) ? v : NEG_INF);
+          for (int hd = 0; hd < 4; ++hd) v += wv[mt][hd] * relu1(FMT == 1 ? acc[hd] * ksc : acc[hd]);
+          rmax[mt] = fmaxf(rmax[mt], (full || (t >= t_lo && t <= hi[mt])) ? v : NEG_INF);
+        }
       }
-    }
-    if (h == 1) {
+    };
+
+    // The wave takes its pages from its last valid one down (page i_last, then
+    // i_last - 1, ..., then the pages past the context, which score -inf).
+    // The step's new index rows (positions L - q .. L - 1; their stores into
+    // the pages are side work) sit in the last valid page(s), so the wave that
+    // holds them meets them in its first chunks. Its workgroup's waves
+    // quantize them while their first copies are in flight, and the wave
+    // writes them over the chunk's LDS copy (in the copy layout) once the copy
+    // has landed, before scoring it.
+    const int i_last = min(lim - 1 - p0, PPW - 1);
+    auto page_of = [&](int o) { return (i_last - o + PPW) % PPW; };   // order o -> page index
+    const bool own = st.idx_new != nullptr && L >= 1 && L - 1 >= p0 * kTokens && max(L - q, 0) < (p0 + PPW) * kTokens;
+
+    // ---- the chunk pipeline. The waits are explicit (the compiler does not
+    // order LDS reads after direct-to-LDS loads): vmcnt counts this wave's
+    // vector memory operations in issue order, so "at most n chunks' copies
+    // outstanding" right after issuing chunk u + n means every older operation
+    // — chunk u's copies included — is done. Stage (u + S - 1) % S is refilled
+    // only after chunk u - 1, which it held, has been computed.
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const float r = max16_dpp(rmax[mt]);
-        const int jw = 4 * mt + kg;
-        if (n == 0 && jw < q && p < c.stride) srow[(int64_t)jw * c.stride + p] = valid[i] ? r : NEG_INF;
+    for (int u = 0; u < S - 1; ++u)
+      dma_chunk<FMT>(stage_at(wave, u), c.idx_pages + (int64_t)phys_of(page_of(u >> 1)) * CK::kPage, u & 1, n, kg,
+                     lane);
+    quant_share();
+    float rmax[MT];
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+      const int i = page_of(u >> 1), h = u & 1;
+      const int p = p0 + i;
+      uint8_t *stage = stage_at(wave, u % S);
+      if (u + S - 1 < kUnits) {
+        const int un = u + S - 1;
+        dma_chunk<FMT>(stage_at(wave, un % S), c.idx_pages + (int64_t)phys_of(page_of(un >> 1)) * CK::kPage, un & 1,
+                       n, kg, lane);
+      }
+      wait_chunks<CK::kDma, S - 1>(min(S - 1, kUnits - 1 - u));
+      if (u < 4 && own) {                            // the new rows are in the first two pages taken
+        const int c0 = p * kTokens + 64 * h;         // the chunk's first position
+#pragma unroll
+        for (int j = 0; j < 4 * MT; ++j) {
+          const int t = L - q + j;
+          if (j < q && t >= c0 && t <= c0 + 63) patch_row<FMT>(stage, t - c0, s_qc[64 * j + lane], s_qw[j], lane);
+        }
+      }
+      if (h == 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) rmax[mt] = NEG_INF;
+      }
+      chunk_max(stage, p, h, p * kTokens + 64 * h + 63 <= pos_min, INT32_MIN, posw, rmax);
+      if (h == 1) {
+        const bool ok = valid_of(i);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const float r = max16_dpp(rmax[mt]);
+          const int jw = 4 * mt + kg;
+          if (n == 0 && jw < q && p < c.stride) srow[(int64_t)jw * c.stride + p] = ok ? r : NEG_INF;
+        }
       }
     }
   }
+  side_finish(c, st, b, q, L, gw, n_waves, lane, sw);
+}
+
+template <int FMT, int MT, class SH>
+static void launch_shape(const CacheView &c, const uint16_t *q_idx, const float *w, int32_t B, int32_t q,
+                         int32_t H_I, float *scores, const StepStore &st, hipStream_t s) {
+  const dim3 grid((unsigned)B, (unsigned)((c.stride + SH::kWaves * SH::kPages - 1) / (SH::kWaves * SH::kPages)));
+  hipLaunchKernelGGL((k_index_score<MT, FMT, SH::kWaves, SH::kPages, SH::kStages>), grid, dim3(64 * SH::kWaves), 0,
+                     s, c, q_idx, w, q, H_I, scores, st);
 }
 
 template <int FMT, int MT>
-static void launch_shape(const CacheView &c, const uint16_t *q_idx, const float *w, int32_t B, int32_t q,
-                         int32_t H_I, float *scores, const StepStore &st, hipStream_t s) {
-  using SH = ScoreShape<FMT>;
-  const dim3 grid((unsigned)((c.stride + SH::kWaves * SH::kPages - 1) / (SH::kWaves * SH::kPages)), (unsigned)B);
-  hipLaunchKernelGGL((k_index_score<MT, FMT, SH::kWaves, SH::kPages, SH::kStages>), grid, dim3(64 * SH::kWaves), 0,
-                     s, c, q_idx, w, q, H_I, scores, st);
+static void launch_mt(const CacheView &c, const uint16_t *q_idx, const float *w, int32_t B, int32_t q,
+                      int32_t H_I, float *scores, const StepStore &st, hipStream_t s) {
+  const int64_t pages = (int64_t)B * c.stride;
+  if constexpr (FMT == 1) {               // 8.25 KiB chunks: two stages of four waves, two workgroups per CU
+    launch_shape<FMT, MT, Shape<4, 2, 2>>(c, q_idx, w, B, q, H_I, scores, st, s);
+  } else if (pages >= 256 * 32) {         // >= 256 workgroups of 32 pages
+    launch_shape<FMT, MT, Shape<4, 8, 3>>(c, q_idx, w, B, q, H_I, scores, st, s);
+  } else if (pages >= 256 * 16) {
+    launch_shape<FMT, MT, Shape<4, 4, 2>>(c, q_idx, w, B, q, H_I, scores, st, s);
+  } else {
+    launch_shape<FMT, MT, Shape<4, 1, 2>>(c, q_idx, w, B, q, H_I, scores, st, s);
+  }
 }
 
 template <int FMT>
 static void launch_fmt(const CacheView &c, const uint16_t *q_idx, const float *w, int32_t B, int32_t q,
                        int32_t H_I, float *scores, const StepStore &st, hipStream_t s) {
   switch ((4 * q + 15) / 16) {                      // M tiles: 4 A-rows per query row
-    case 1: launch_shape<FMT, 1>(c, q_idx, w, B, q, H_I, scores, st, s); break;
-    case 2: launch_shape<FMT, 2>(c, q_idx, w, B, q, H_I, scores, st, s); break;
-    case 3: launch_shape<FMT, 3>(c, q_idx, w, B, q, H_I, scores, st, s); break;
-    default: launch_shape<FMT, 4>(c, q_idx, w, B, q, H_I, scores, st, s); break;
+    case 1: launch_mt<FMT, 1>(c, q_idx, w, B, q, H_I, scores, st, s); break;
+    case 2: launch_mt<FMT, 2>(c, q_idx, w, B, q, H_I, scores, st, s); break;
+    case 3: launch_mt<FMT, 3>(c, q_idx, w, B, q, H_I, scores, st, s); break;
+    default: launch_mt<FMT, 4>(c, q_idx, w, B, q, H_I, scores, st, s); break;
   }
 }
 
