@@ -97,7 +97,7 @@ int default_partitions(int32_t topk) {
 
 // workspace segments of decode_step, in order
 struct StepWs {
-  size_t scores, table, q8, sp_m, sp_l, sp_o, total;
+  size_t scores, table, q8, sp_m, sp_l, sp_o, counters, total;
 };
 
 StepWs step_ws(int32_t B, int32_t q, int32_t H, int32_t topk, int32_t stride, int32_t P) {
@@ -110,6 +110,7 @@ StepWs step_ws(int32_t B, int32_t q, int32_t H, int32_t topk, int32_t stride, in
   w.sp_m = off;   off += round_up(rows * H * P * sizeof(float));
   w.sp_l = off;   off += round_up(rows * H * P * sizeof(float));
   w.sp_o = off;   off += round_up(rows * H * P * MXS_HEAD_DIM * sizeof(float));
+  w.counters = off; off += round_up(rows * sizeof(uint32_t));
   w.total = off;
   return w;
 }
@@ -329,14 +330,16 @@ int decode_step(const mxs_step *a, void *ws, size_t ws_bytes, void *stream) {
   float *sp_m = reinterpret_cast<float *>(base + w.sp_m);
   float *sp_l = reinterpret_cast<float *>(base + w.sp_l);
   float *sp_o = reinterpret_cast<float *>(base + w.sp_o);
+  uint32_t *counters = reinterpret_cast<uint32_t *>(base + w.counters);
   const hipStream_t s = (hipStream_t)stream;
   const mxs::CacheView c = view(cache);
 
   // 1 - 3: the new rows into the pages, q -> e4m3 and the scores, one launch
   // (the waves that own a page holding new positions store those index rows
   // before scoring it; K / V rows and q are read only by the attention
-  // launch)
+  // launch); it also clears the attention launch's per-row merge counters
   mxs::StepStore st;
+  st.counters = counters;
   if (store) {
     st.k_new = a->k_new;
     st.v_new = a->v_new;
@@ -351,17 +354,18 @@ int decode_step(const mxs_step *a, void *ws, size_t ws_bytes, void *stream) {
   if (int r = launched(mxs::launch_index_score(c, a->q_idx, a->w, a->B, a->q, a->H_I, scores, st, s),
                        "decode_step: store + score"))
     return r;
-  // 4 + 5: top-k and split attention, one launch: every attention workgroup
-  // selects its row's blocks from the scores itself (partition 0 writes the
-  // row's block table)
+  // 4 - 6: top-k, split attention and merge, one launch: every attention
+  // workgroup selects its row's blocks from the scores itself (partition 0
+  // writes the row's block table), and the row's last partition to finish
+  // merges the row
   const void *qa = mx ? static_cast<const void *>(q8) : a->query;
-  if (int r = launched(mxs::launch_select_attn(c, scores, qa, a->B, a->q, a->H, a->topk, P, a->sm_scale, table, sp_m,
-                                               sp_l, sp_o, s),
-                       "decode_step: top-k + split attention"))
-    return r;
-  // 6: merge
-  return launched(mxs::launch_lse_merge(sp_m, sp_l, sp_o, a->B * a->q * a->H, P, a->out, a->lse, s),
-                  "decode_step: merge");
+  mxs::FusedMerge fm;
+  fm.counters = counters;
+  fm.out = a->out;
+  fm.lse = a->lse;
+  return launched(mxs::launch_select_attn(c, scores, qa, a->B, a->q, a->H, a->topk, P, a->sm_scale, table, sp_m, sp_l,
+                                          sp_o, fm, s),
+                  "decode_step: top-k + split attention + merge");
 }
 
 }  // extern "C"

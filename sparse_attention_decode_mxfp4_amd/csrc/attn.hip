@@ -38,6 +38,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "topk.hpp"
+#include "merge.hpp"
 
 namespace mxs {
 
@@ -246,8 +247,19 @@ __device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t
   }
 }
 
+// A partial value stored device-coherent (COHERENT: an agent-scope store,
+// visible to every XCD once the wave's stores are done) or plainly.
+template <bool COHERENT>
+__device__ __forceinline__ void put(float *p, float v) {
+  if constexpr (COHERENT)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+
 // This wave's sums for head n, then the 4-wave merge through LDS into the
 // workgroup's partial (m, l, O) of partition p.
+template <bool COHERENT>
 __device__ __forceinline__ void write_partial(float (&s_m)[kAttnWaves][16], float (&s_l)[kAttnWaves][16],
                                               float (&s_o)[kAttnWaves][16][kDim + 4], float m_run, float l_run,
                                               const f32x4 O[8], int row, int H, int P, int p, float *__restrict__ sp_m,
@@ -261,7 +273,7 @@ __device__ __forceinline__ void write_partial(float (&s_m)[kAttnWaves][16], floa
     s_m[wave][n] = m_run;
     s_l[wave][n] = l_run;
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int h = 4 * kg + i;
@@ -273,7 +285,7 @@ __device__ __forceinline__ void write_partial(float (&s_m)[kAttnWaves][16], floa
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) s_o[wave][h][8 * n + dt] = O[dt][i] * f;
   }
-  __syncthreads();
+  lds_barrier();
   const int64_t part = (int64_t)row * H;      // + h, then * P + p
 #pragma unroll
   for (int rr = 0; rr < 8; ++rr) {
@@ -283,7 +295,7 @@ __device__ __forceinline__ void write_partial(float (&s_m)[kAttnWaves][16], floa
       float o = 0.f;
 #pragma unroll
       for (int w = 0; w < kAttnWaves; ++w) o += s_o[w][h][d];
-      sp_o[((part + h) * P + p) * kDim + d] = o;
+      put<COHERENT>(sp_o + ((part + h) * P + p) * kDim + d, o);
     }
   }
   if (threadIdx.x < (unsigned)H) {
@@ -295,8 +307,8 @@ __device__ __forceinline__ void write_partial(float (&s_m)[kAttnWaves][16], floa
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w)
       Lsum += (s_m[w][h] == NEG_INF) ? 0.0f : s_l[w][h] * __expf(s_m[w][h] - M);
-    sp_m[(part + h) * P + p] = M;
-    sp_l[(part + h) * P + p] = Lsum;
+    put<COHERENT>(sp_m + (part + h) * P + p, M);
+    put<COHERENT>(sp_l + (part + h) * P + p, Lsum);
   }
 }
 
@@ -329,25 +341,28 @@ __global__ __launch_bounds__(256) void k_split_attn(CacheView c, const void *__r
     if (phys < 0 || phys >= c.num_pages) continue;
     attend_block<FMT>(c, phys, blk * kTokens, pos, qbf, sm_scale, m_run, l_run, O, n, kg);
   }
-  write_partial(s_m, s_l, s_o, m_run, l_run, O, row, H, P, p, sp_m, sp_l, sp_o);
+  write_partial<false>(s_m, s_l, s_o, m_run, l_run, O, row, H, P, p, sp_m, sp_l, sp_o);
 }
 
 // The decode step's attention: the workgroup first selects its row's top-k
 // blocks itself (the workgroup selection of topk.hpp over the row's scores),
 // with the row's page table staged in LDS, then attends to the slots of its
 // partition. Everything it needs from memory before the K / V pages — the
-// context length, the score row, the page-table row and the query — is
-// requested in one round trip. Partition 0 also writes the row's block table.
+// context length, the score row and the page-table row — is requested in one
+// round trip; the query goes out with the first block's pages. Partition 0
+// also writes the row's block table.
 template <int FMT, int ITEMS>
 __global__ __launch_bounds__(256) void k_select_attn(CacheView c, const float *__restrict__ scores,
                                                      const void *__restrict__ qv, int32_t q_rows, int32_t H,
                                                      int32_t topk, int32_t P, float sm_scale,
                                                      int32_t *__restrict__ block_table, float *__restrict__ sp_m,
-                                                     float *__restrict__ sp_l, float *__restrict__ sp_o) {
+                                                     float *__restrict__ sp_l, float *__restrict__ sp_o,
+                                                     FusedMerge fm) {
   __shared__ TopkSmem<ITEMS> tk;
   __shared__ int32_t s_pt[kTopkThreads * ITEMS];
   __shared__ float s_m[kAttnWaves][16], s_l[kAttnWaves][16];
   __shared__ float s_o[kAttnWaves][16][kDim + 4];
+  __shared__ uint32_t s_last;
   const int p = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int row = b * q_rows + j;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -363,9 +378,6 @@ __global__ __launch_bounds__(256) void k_select_attn(CacheView c, const float *_
     v[r] = scores[(int64_t)row * stride + i];
     pt[r] = c.page_table[(int64_t)b * stride + i];
   }
-  bf16x8 qbf[4];
-  load_query<FMT>(qv, row, H, n, kg, qbf);
-
   const int pos = L - q_rows + j;
   const int n_cand = pos < 0 ? 0 : min(pos / kTokens + 1, stride);
 #pragma unroll
@@ -373,11 +385,13 @@ __global__ __launch_bounds__(256) void k_select_attn(CacheView c, const float *_
     if (tid + kTopkThreads * r < stride) s_pt[tid + kTopkThreads * r] = pt[r];
   int n_sel;
   const uint32_t sel = wg_topk<ITEMS>(v, n_cand, topk, tk, n_sel);
-  __syncthreads();                                 // s_pt (the selection may return before any barrier)
+  lds_barrier();                                   // s_pt (the selection may return before any barrier)
   if (p == 0 && tid < topk) block_table[(int64_t)row * topk + tid] = tid < n_sel ? (int32_t)sel : -1;
 
   const int cps = (topk + P - 1) / P;
   const int slot0 = p * cps, slot1 = min(slot0 + cps, n_sel);
+  bf16x8 qbf[4];                                   // requested with the first block's pages
+  load_query<FMT>(qv, row, H, n, kg, qbf);
   float m_run = -__builtin_inff(), l_run = 0.0f;
   f32x4 O[8];
 #pragma unroll
@@ -388,7 +402,22 @@ __global__ __launch_bounds__(256) void k_select_attn(CacheView c, const float *_
     if (phys < 0 || phys >= c.num_pages) continue;
     attend_block<FMT>(c, phys, blk * kTokens, pos, qbf, sm_scale, m_run, l_run, O, n, kg);
   }
-  write_partial(s_m, s_l, s_o, m_run, l_run, O, row, H, P, p, sp_m, sp_l, sp_o);
+  write_partial<true>(s_m, s_l, s_o, m_run, l_run, O, row, H, P, p, sp_m, sp_l, sp_o);
+
+  // ---- the row's merge, by its last partition workgroup to finish. The
+  // partials went out as agent-scope (device-coherent) stores; once every
+  // wave's stores are done (vmcnt) and the workgroup has met, one arrival is
+  // counted (device-scope atomic). The workgroup that takes the count to P
+  // reads every partition's partials with agent-scope loads. No cache
+  // write-back or invalidate is needed on either side.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(fm.counters + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (uint32_t)(P - 1);
+  lds_barrier();
+  if (!s_last) return;
+  merge_row<true>(sp_m, sp_l, sp_o, row, H, P, fm.out, fm.lse);
 }
 
 hipError_t launch_split_attn(const CacheView &c, const void *q, int q_dtype, const int32_t *block_table,
@@ -408,12 +437,12 @@ hipError_t launch_split_attn(const CacheView &c, const void *q, int q_dtype, con
 
 hipError_t launch_select_attn(const CacheView &c, const float *scores, const void *q, int32_t B, int32_t q_rows,
                               int32_t H, int32_t topk, int32_t P, float sm_scale, int32_t *block_table, float *sp_m,
-                              float *sp_l, float *sp_o, hipStream_t s) {
+                              float *sp_l, float *sp_o, const FusedMerge &fm, hipStream_t s) {
   if (B * q_rows == 0) return hipSuccess;
   const dim3 grid((unsigned)P, (unsigned)q_rows, (unsigned)B), block(kTopkThreads);
 #define MXS_SELECT_ATTN(F, I)                                                                                   \
   hipLaunchKernelGGL((k_select_attn<F, I>), grid, block, 0, s, c, scores, q, q_rows, H, topk, P, sm_scale,     \
-                     block_table, sp_m, sp_l, sp_o)
+                     block_table, sp_m, sp_l, sp_o, fm)
   if (c.kv_format == 0) {
     if (c.stride <= kTopkThreads * 2) MXS_SELECT_ATTN(0, 2);
     else if (c.stride <= kTopkThreads * 8) MXS_SELECT_ATTN(0, 8);

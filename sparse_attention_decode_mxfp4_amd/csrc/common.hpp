@@ -139,17 +139,6 @@ __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
   }
 }
 
-// xor_lane for a mask that is a constant once the caller's loop is unrolled
-__device__ __forceinline__ uint32_t xor_lane_n(uint32_t v, int m) {
-  switch (m) {
-    case 1: return xor_lane<1>(v);
-    case 2: return xor_lane<2>(v);
-    case 4: return xor_lane<4>(v);
-    case 8: return xor_lane<8>(v);
-    case 16: return xor_lane<16>(v);
-    default: return xor_lane<32>(v);
-  }
-}
 
 __device__ __forceinline__ float wave_max16(float v) {      // max over the 16 lanes sharing lane / 16
   v = fmaxf(v, __shfl_xor(v, 1));

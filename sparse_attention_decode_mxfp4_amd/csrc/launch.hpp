@@ -28,6 +28,7 @@ struct StepStore {
   const void *q_att = nullptr;
   int q_dtype = 0, H = 0;
   uint8_t *q8 = nullptr;
+  uint32_t *counters = nullptr;      // [B][q] cleared (the attention launch's merge counters)
 };
 
 // index scores (score.hip)
@@ -46,10 +47,17 @@ hipError_t launch_split_attn(const CacheView &c, const void *q, int q_dtype,
 
 // the decode step's attention (attn.hip): each workgroup selects its row's
 // top-k blocks from the scores [B][q_rows][stride] itself, writes the row's
-// block table (partition 0) and attends to its partition's slots
+// block table (partition 0) and attends to its partition's slots; the row's
+// last partition to finish merges the row into out / lse (counters [B][q_rows]
+// zero on entry: the scorer launch clears them)
+struct FusedMerge {
+  uint32_t *counters = nullptr;
+  uint16_t *out = nullptr;
+  float *lse = nullptr;
+};
 hipError_t launch_select_attn(const CacheView &c, const float *scores, const void *q, int32_t B, int32_t q_rows,
                               int32_t H, int32_t topk, int32_t P, float sm_scale, int32_t *block_table, float *sp_m,
-                              float *sp_l, float *sp_o, hipStream_t s);
+                              float *sp_l, float *sp_o, const FusedMerge &fm, hipStream_t s);
 
 // merge (merge.hip)
 hipError_t launch_lse_merge(const float *sp_m, const float *sp_l, const float *sp_o, int32_t n_rows,

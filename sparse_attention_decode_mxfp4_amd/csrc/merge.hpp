@@ -10,16 +10,37 @@
 
 namespace mxs {
 
+// COHERENT: the partials are read with agent-scope loads (written by other
+// workgroups of the same launch with agent-scope stores).
+template <bool COHERENT>
+__device__ __forceinline__ float get(const float *p) {
+  if constexpr (COHERENT)
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    return *p;
+}
+template <bool COHERENT>
+__device__ __forceinline__ float2 get2(const float2 *p) {
+  if constexpr (COHERENT) {
+    const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(u2f((uint32_t)u), u2f((uint32_t)(u >> 32)));
+  } else {
+    return *p;
+  }
+}
+
+template <bool COHERENT = false>
 __device__ __forceinline__ void merge_one(const float *__restrict__ sp_m, const float *__restrict__ sp_l,
                                           const float *__restrict__ sp_o, int64_t r, int32_t P, int lane,
                                           uint16_t *__restrict__ out, float *__restrict__ lse) {
   const float NEG_INF = -__builtin_inff();
-  const float mraw = sp_m[r * P + min(lane, P - 1)];
-  const float lraw = sp_l[r * P + min(lane, P - 1)];
+  const float mraw = get<COHERENT>(sp_m + r * P + min(lane, P - 1));
+  const float lraw = get<COHERENT>(sp_l + r * P + min(lane, P - 1));
   const float2 *po = reinterpret_cast<const float2 *>(sp_o + r * P * kDim) + lane;
   float2 v[8];                                  // the first 8 partitions' outputs, requested with (m, l)
 #pragma unroll
-  for (int u = 0; u < 8; ++u) v[u] = po[min(u, P - 1) * (kDim / 2)];   // clamped: no branch
+  for (int u = 0; u < 8; ++u) v[u] = get2<COHERENT>(po + min(u, P - 1) * (kDim / 2));   // clamped: no branch
   const float mp = lane < P ? mraw : NEG_INF;
   float M = mp;
 #pragma unroll
@@ -33,7 +54,7 @@ __device__ __forceinline__ void merge_one(const float *__restrict__ sp_m, const 
   for (int p0 = 0; p0 < P; p0 += 8) {
     if (p0 > 0) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = po[min(p0 + u, P - 1) * (kDim / 2)];
+      for (int u = 0; u < 8; ++u) v[u] = get2<COHERENT>(po + min(p0 + u, P - 1) * (kDim / 2));
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -51,6 +72,74 @@ __device__ __forceinline__ void merge_one(const float *__restrict__ sp_m, const 
   const uint32_t b1 = (u1 + 0x7FFFu + ((u1 >> 16) & 1u)) >> 16;
   reinterpret_cast<uint32_t *>(out + r * kDim)[lane] = b0 | (b1 << 16);
   if (lse && lane == 0) lse[r] = Lp > 0.0f ? M + __logf(Lp) : NEG_INF;
+}
+
+}  // namespace mxs
+
+namespace mxs {
+
+// One query row (H <= 16 heads) merged by a 256-thread workgroup: thread t
+// takes head t / 16 and output elements 8 (t % 16) .. + 7. Every partition's
+// (m, l) and the thread's 8 elements of every partition's O are requested at
+// once, 8 partitions per round (more partitions fold in with an online
+// rescale), so the merge costs one memory round trip for P <= 8.
+template <bool COHERENT>
+__device__ __forceinline__ void merge_row(const float *__restrict__ sp_m, const float *__restrict__ sp_l,
+                                          const float *__restrict__ sp_o, int64_t row, int32_t H, int32_t P,
+                                          uint16_t *__restrict__ out, float *__restrict__ lse) {
+  const float NEG_INF = -__builtin_inff();
+  const int t = threadIdx.x, h = t >> 4, e0 = 8 * (t & 15);
+  if (h >= H) return;
+  const int64_t r = row * H + h;
+  float M = NEG_INF, Lsum = 0.f, acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int p0 = 0; p0 < P; p0 += 8) {
+    float m[8], l[8];
+    float2 o[8][4];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {                 // clamped, unconditional; u >= P - p0 weigh nothing
+      const int pp = min(p0 + u, P - 1);
+      m[u] = get<COHERENT>(sp_m + r * P + pp);
+      l[u] = get<COHERENT>(sp_l + r * P + pp);
+      const float2 *po = reinterpret_cast<const float2 *>(sp_o + (r * P + pp) * kDim + e0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[u][k] = get2<COHERENT>(po + k);
+    }
+    float Mc = M;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) Mc = (p0 + u < P) ? fmaxf(Mc, m[u]) : Mc;
+    const float a = (M == NEG_INF) ? 0.0f : __expf(M - Mc);    // rescale what is folded in so far
+    Lsum *= a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= a;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float wu = (p0 + u < P && m[u] != NEG_INF) ? __expf(m[u] - Mc) : 0.0f;
+      if (wu != 0.0f) {
+        Lsum += l[u] * wu;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[2 * k] += wu * o[u][k].x;
+          acc[2 * k + 1] += wu * o[u][k].y;
+        }
+      }
+    }
+    M = Mc;
+  }
+  const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+  uint32_t packed[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t u0 = f2u(acc[2 * k] * inv), u1 = f2u(acc[2 * k + 1] * inv);
+    const uint32_t b0 = (u0 + 0x7FFFu + ((u0 >> 16) & 1u)) >> 16;   // round to nearest even
+    const uint32_t b1 = (u1 + 0x7FFFu + ((u1 >> 16) & 1u)) >> 16;
+    packed[k] = b0 | (b1 << 16);
+  }
+  uint32_t *dst = reinterpret_cast<uint32_t *>(out + r * kDim + e0);   // out: 4-byte aligned
+#pragma unroll
+  for (int k = 0; k < 4; ++k) dst[k] = packed[k];
+  if (lse && (t & 15) == 0) lse[r] = Lsum > 0.0f ? M + __logf(Lsum) : NEG_INF;
 }
 
 }  // namespace mxs

@@ -17,10 +17,11 @@
 //      (bitonic half-cleaners), so no wave waits for another beyond one barrier;
 //   2. every candidate with key >= T0 (typically a few dozen) is compacted
 //      into LDS (per-wave ballot offsets, one barrier for the wave totals);
-//   3. when at most 64 survive, every wave sorts them by (key descending, id
-//      ascending) across its lanes, keeps the first k and sorts those ids
-//      ascending; with more survivors (ties at the bound) each survivor is
-//      ranked against all of them through LDS first.
+//   3. exactly k survivors are the selection; when at most 64 survive, every
+//      wave sorts them by (key descending, id ascending) across its lanes and
+//      keeps the first k; with more survivors (ties at the bound) each
+//      survivor is ranked against all of them through LDS first; the selected
+//      ids are sorted ascending across the lanes.
 // All cross-lane exchanges are DPP row permutes and gfx950 permlane swaps
 // (no LDS round trip per step).
 #pragma once
@@ -37,50 +38,67 @@ __device__ __forceinline__ uint32_t order_key(float f) {        // branch-free
   return (u & 0x7FFFFFFFu) > 0x7F800000u ? 1u : k;          // NaN: below every number
 }
 
-// Bitonic sort of one value per lane across the 64 lanes (DESC: lane 0 holds
-// the largest).
-template <bool DESC>
-__device__ __forceinline__ uint32_t sort64(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-    for (int st = size >> 1; st > 0; st >>= 1) {
-      const uint32_t o = xor_lane_n(v, st);
-      const bool lower = (lane & st) == 0;
-      const bool first = ((lane & size) == 0) == DESC;     // this block's order is the final one
-      v = (lower == first) ? max(v, o) : min(v, o);
-    }
+// Bitonic networks across the 64 lanes, one value per lane, written as
+// template recursion so that every step's lane permute is a compile-time
+// choice (a runtime loop over the step distance would dispatch each
+// permute through branches).
+//
+// One stage of the network for blocks of SIZE lanes: compare-exchange at
+// distances ST, ST / 2, ..., 1; a block sorts in the final order (DESC: lane
+// 0 largest) when (lane & SIZE) == 0 and the other way otherwise (for SIZE =
+// 64 every block sorts in the final order: a merge).
+template <bool DESC, int SIZE, int ST>
+__device__ __forceinline__ uint32_t bitonic_stage(uint32_t v, int lane) {
+  if constexpr (ST == 0) {
+    return v;
+  } else {
+    const uint32_t o = xor_lane<ST>(v);
+    const bool lower = (lane & ST) == 0;
+    const bool first = ((lane & SIZE) == 0) == DESC;
+    return bitonic_stage<DESC, SIZE, ST / 2>((lower == first) ? max(v, o) : min(v, o), lane);
   }
-  return v;
 }
 
-__device__ __forceinline__ uint64_t sort64_desc_u64(uint64_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-    for (int st = size >> 1; st > 0; st >>= 1) {
-      const uint64_t o = ((uint64_t)xor_lane_n((uint32_t)(v >> 32), st) << 32) | xor_lane_n((uint32_t)v, st);
-      const bool lower = (lane & st) == 0;
-      const bool first = (lane & size) == 0;
-      v = (lower == first) ? (v > o ? v : o) : (v < o ? v : o);
-    }
+template <bool DESC, int SIZE = 2>
+__device__ __forceinline__ uint32_t sort64(uint32_t v) {
+  if constexpr (SIZE > 64) {
+    return v;
+  } else {
+    return sort64<DESC, SIZE * 2>(bitonic_stage<DESC, SIZE, SIZE / 2>(v, threadIdx.x & 63));
   }
-  return v;
 }
 
 // A bitonic sequence across the 64 lanes -> sorted.
 template <bool DESC>
 __device__ __forceinline__ uint32_t merge64(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int st = 32; st > 0; st >>= 1) {
-    const uint32_t o = xor_lane_n(v, st);
-    v = (((lane & st) == 0) == DESC) ? max(v, o) : min(v, o);
-  }
-  return v;
+  return bitonic_stage<DESC, 64, 32>(v, threadIdx.x & 63);
 }
+
+template <int SIZE, int ST>
+__device__ __forceinline__ uint64_t bitonic_stage_desc_u64(uint64_t v, int lane) {
+  if constexpr (ST == 0) {
+    return v;
+  } else {
+    const uint64_t o = ((uint64_t)xor_lane<ST>((uint32_t)(v >> 32)) << 32) | xor_lane<ST>((uint32_t)v);
+    const bool lower = (lane & ST) == 0;
+    const bool first = (lane & SIZE) == 0;
+    return bitonic_stage_desc_u64<SIZE, ST / 2>((lower == first) ? (v > o ? v : o) : (v < o ? v : o), lane);
+  }
+}
+
+template <int SIZE = 2>
+__device__ __forceinline__ uint64_t sort64_desc_u64(uint64_t v) {
+  if constexpr (SIZE > 64) {
+    return v;
+  } else {
+    return sort64_desc_u64<SIZE * 2>(bitonic_stage_desc_u64<SIZE, SIZE / 2>(v, threadIdx.x & 63));
+  }
+}
+
+// Workgroup barrier for LDS data only: the LDS writes are waited for, vector
+// memory operations are not (unlike __syncthreads, which would also wait for
+// every global load still in flight).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int ITEMS>
 struct TopkSmem {
@@ -114,7 +132,7 @@ __device__ __forceinline__ uint32_t wg_topk(const float (&v)[ITEMS], int n_cand,
   }
   // 1. T0: the k-th largest of the 256 thread maxima
   sm.wmax[wave][lane] = sort64<true>(m);
-  __syncthreads();
+  lds_barrier();
   const uint32_t c = merge64<true>(max(sm.wmax[0][lane], sm.wmax[1][63 - lane]));   // top 64 of waves 0, 1
   const uint32_t d = merge64<false>(max(sm.wmax[2][lane], sm.wmax[3][63 - lane]));  // of waves 2, 3, ascending
   const uint32_t e = merge64<true>(max(c, d));                                        // of all four
@@ -132,7 +150,7 @@ __device__ __forceinline__ uint32_t wg_topk(const float (&v)[ITEMS], int n_cand,
     wave_n += (uint32_t)__popcll(bal);
   }
   if (lane == 0) sm.wtot[wave] = wave_n;
-  __syncthreads();
+  lds_barrier();
   uint32_t base = 0, n_surv = 0;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -147,11 +165,13 @@ __device__ __forceinline__ uint32_t wg_topk(const float (&v)[ITEMS], int n_cand,
       sm.idx[base + at[r]] = (uint16_t)(tid + kTopkThreads * r);
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // 3. exact selection by (key descending, id ascending)
   uint32_t sel;
-  if (n_surv <= 64u) {
+  if (n_surv == (uint32_t)topk) {            // exactly k survive: all selected
+    sel = (uint32_t)lane < n_surv ? (uint32_t)sm.idx[lane] : 0xFFFFFFFFu;
+  } else if (n_surv <= 64u) {
     const bool have = (uint32_t)lane < n_surv;
     const uint32_t ks = have ? sm.key[lane] : 0u, is = have ? (uint32_t)sm.idx[lane] : 0u;
     const uint64_t comp = sort64_desc_u64(have ? (((uint64_t)ks << 32) | (0xFFFFFFFFu - is)) : 0ull);
@@ -166,7 +186,7 @@ __device__ __forceinline__ uint32_t wg_topk(const float (&v)[ITEMS], int n_cand,
       }
       if (rank < (uint32_t)topk) sm.by_rank[rank] = ii;
     }
-    __syncthreads();
+    lds_barrier();
     sel = lane < topk ? sm.by_rank[lane] : 0xFFFFFFFFu;
   }
   return sort64<false>(sel);                 // ascending ids
