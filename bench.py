@@ -36,6 +36,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 PAGE_MX = 8704
+CSRC = os.path.join(ROOT, "sparse_attention_decode_mxfp4_amd", "csrc")
+# the sources the index scorer kernel is built from; the HBM traffic measured
+# with rocprofv3 counters is reported only while they are unchanged
+SCORER_SOURCES = ("score.hip", "common.hpp", "rowstore.hpp", "launch.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scorer_traffic.json")
 
 
 def log(*a):
@@ -61,6 +66,42 @@ def algorithmic_bytes(inp, table: np.ndarray) -> dict:
     return {"index_pages": idx_pages * PAGE_MX, "kv_pages": 2 * kv_pages * PAGE_MX, "other": other,
             "total": idx_pages * PAGE_MX + 2 * kv_pages * PAGE_MX + other,
             "n_index_pages": idx_pages, "n_kv_pages": 2 * kv_pages}
+
+
+def scorer_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in SCORER_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per scorer launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy's reading), or None
+    when there is none for this workload or the scorer changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("scorer_sources_sha256") != scorer_source_hash():
+        return None
+    return t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
+
+
+def copy_calibration(n_bytes: int = 256 << 20, reps: int = 20):
+    """A plain device copy of known size, for scaling rocprofv3's FETCH_SIZE /
+    WRITE_SIZE readings: each launch reads and writes n_bytes."""
+    import torch
+    src = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_launch": n_bytes, "bytes_written_per_launch": n_bytes,
+                                           "launches": reps}}), flush=True)
 
 
 def cpu_baseline(inp, min_seconds=10.0, max_seconds=30.0) -> dict:
@@ -96,6 +137,8 @@ def main():
     ap.add_argument("--scorer-launches", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain copy of known size (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -104,6 +147,9 @@ def main():
                                    "single-GPU kernel chain with no collectives; run with --gpus 1"}))
         sys.exit(2)
 
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
     import sparse_attention_decode_mxfp4_amd as mx
     import workloads as W
@@ -237,7 +283,8 @@ def main():
         "warm_mall_ms_per_step": warm_ms,
         "roofline": {"bound": "hbm", "kernel": "index scorer (k_index_score)", "achieved": score_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": score_gbps / HBM_PEAK_GBPS,
-                     "traffic": None, "avg_launch_us": score_us, "algorithmic_bytes_per_launch": score_bytes},
+                     "traffic": measured_traffic(wl.name), "avg_launch_us": score_us,
+                     "algorithmic_bytes_per_launch": score_bytes},
     }
     log(f"[bench] step {ms_step * 1e3:.1f} us (events {ev_ms_step * 1e3:.1f} us, warm {warm_ms * 1e3:.1f} us), "
         f"{step_gbps:.0f} GB/s; scorer {score_us:.1f} us = {score_gbps:.0f} GB/s")

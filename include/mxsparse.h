@@ -211,9 +211,14 @@ typedef struct {
     float *scores_out;         /* [B][q][page_table_stride] fp32 or null                */
 } mxs_step;
 
-/* decode_step: the six stages above on one stream. ws: device workspace of at
- * least mxs_workspace_bytes(...) bytes, 256 B aligned; its contents need no
- * initialization and are scratch after the call. */
+/* decode_step: the six stages above on one stream, as two launches: the index
+ * scores (which also store the step's new K / V / index rows and its e4m3
+ * query), then top-k, split attention and the log-sum-exp merge (each row's
+ * last partition workgroup merges the row). ws: device workspace of at least
+ * mxs_workspace_bytes(...) bytes, 256 B aligned; its contents need no
+ * initialization and are scratch after the call (it holds the per-row merge
+ * counters, cleared by the first launch), so two calls in flight at once must
+ * not share one. */
 int decode_step(const mxs_step *step, void *ws, size_t ws_bytes, void *stream);
 size_t mxs_workspace_bytes(int32_t B, int32_t q, int32_t H, int32_t H_I, int32_t topk,
                            int32_t page_table_stride, int32_t num_partitions);
