@@ -44,12 +44,28 @@ namespace mxs {
 
 constexpr int kAttnWaves = 4;
 
-__device__ __forceinline__ uint32_t lo_pair(uint32_t x, uint32_t y) { return (x & 0xFFFFu) | (y << 16); }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t x, uint32_t y) { return (x >> 16) | (y & 0xFFFF0000u); }
-__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {   // fp32 -> bf16, round to nearest even
-  const uint32_t u = f2u(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Half-word pairs of two dwords (v_perm_b32): the low halves of x and y, and
+// the high halves, x's in the low half of the result.
+__device__ __forceinline__ uint32_t lo_pair(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x05040100u); }
+__device__ __forceinline__ uint32_t hi_pair(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x07060302u); }
+// Two fp32 as a bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
+// Four e4m3 codes (one dword) as two dwords of bf16 pairs, element order
+// kept (v_cvt_scalef32_pk_bf16_fp8 with scale 1: exact, e4m3 has 3 mantissa
+// bits; 0x7F / 0xFF give NaN).
+__device__ __forceinline__ uint2 e4m3x4_bf16(uint32_t d) {
+  return make_uint2(bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, false)),
+                    bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, true)));
+}
+// fp32 value of an e8m0 scale byte for the cvt_scalef32 instructions:
+// byte << 23 is 2^(byte - 127) for byte >= 1, and byte 0 takes 0x400000 = 2^-127.
+__device__ __forceinline__ float e8m0_scale(uint32_t byte) { return u2f(max(byte << 23, 0x00400000u)); }
 
 // One block's operands as this lane loads them (all requested before any math).
 //  K: tile nt -> token 16 nt + n; MXFP4: 16 bytes of group kg + its scale byte;
@@ -98,24 +114,38 @@ __device__ __forceinline__ void load_block(BlockRegs<FMT> &r, const uint8_t *kp,
   }
 }
 
-// B operand of QK: head n's query as bf16, elements 32 kg + 8 s .. + 7 for
-// k-step s (the order of the key groups each lane loads). An e4m3 query is
-// widened exactly; a bf16 query is loaded as is. Heads >= H load head 0 and
-// are zeroed (unconditional loads).
+// The lane's query elements for QK, as loaded: head n, elements 32 kg + 8 s
+// .. + 7 for k-step s (the order of the key groups each lane loads); e4m3
+// codes with an MXFP4 cache, bf16 with an FP8 cache. Heads >= H load head 0
+// (unconditional loads) and are zeroed when the operands are formed.
+template <int FMT> struct QueryRegs;
+template <> struct QueryRegs<0> { uint2 c[4]; };
+template <> struct QueryRegs<1> { u32x4 c[4]; };
+
 template <int FMT>
-__device__ __forceinline__ void load_query(const void *__restrict__ qv, int row, int H, int n, int kg, bf16x8 qbf[4]) {
-  const int hq = n < H ? n : 0;
+__device__ __forceinline__ void load_query(const void *__restrict__ qv, int row, int H, int n, int kg,
+                                           QueryRegs<FMT> &q) {
+  const int64_t base = ((int64_t)row * H + (n < H ? n : 0)) * kDim + 32 * kg;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if constexpr (FMT == 0)
+      q.c[s] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint8_t *>(qv) + base + 8 * s);
+    else
+      q.c[s] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(qv) + base + 8 * s);
+  }
+}
+
+// B operand of QK: the query as bf16 (e4m3 widened exactly).
+template <int FMT>
+__device__ __forceinline__ void query_operands(const QueryRegs<FMT> &q, int H, int n, bf16x8 qbf[4]) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     u32x4 v;
     if constexpr (FMT == 0) {
-      const uint2 c8 = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint8_t *>(qv) +
-                                                        ((int64_t)row * H + hq) * kDim + 32 * kg + 8 * s);
-      const uint2 x = e4m3x4_to_bf16(c8.x), y = e4m3x4_to_bf16(c8.y);
+      const uint2 x = e4m3x4_bf16(q.c[s].x), y = e4m3x4_bf16(q.c[s].y);
       v = u32x4{x.x, x.y, y.x, y.y};
     } else {
-      v = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(qv) + ((int64_t)row * H + hq) * kDim +
-                                           32 * kg + 8 * s);
+      v = q.c[s];
     }
     if (n >= H) v = u32x4{0u, 0u, 0u, 0u};
     qbf[s] = __builtin_bit_cast(bf16x8, v);
@@ -123,71 +153,87 @@ __device__ __forceinline__ void load_query(const void *__restrict__ qv, int row,
 }
 
 // One selected block (page `phys`, first token position t0) folded into this
-// wave's online softmax state (m_run, l_run, O) for head n = lane % 16.
-template <int FMT>
-__device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t0, int pos, const bf16x8 qbf[4],
-                                             float sm_scale, float &m_run, float &l_run, f32x4 O[8], int n, int kg) {
+// wave's online softmax state for head n = lane % 16: m_run (log2 units: the
+// logits times log2 e), l_run, O. FULL: every token of the block is at or
+// before the row's position (no masking). FIRST: the wave's first block
+// (nothing to rescale). `phys` is wave-uniform.
+template <int FMT, bool FULL, bool FIRST>
+__device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t0, int pos, const QueryRegs<FMT> &q,
+                                             int H, float qk_scale2, float &m_run, float &l_run, f32x4 O[8], int n,
+                                             int kg) {
   const float NEG_INF = -__builtin_inff();
   const int64_t pb = (int64_t)phys * (FMT == 0 ? kMxPageBytes : kF8PageBytes);
   BlockRegs<FMT> r;
   load_block<FMT>(r, c.k_pages + pb, c.v_pages + pb, n, kg);
+  // The query is widened here, after the pages are requested: the empty asm
+  // keeps the (loop-invariant) widening from being hoisted above these loads,
+  // which would wait for the query before any page is requested.
+  QueryRegs<FMT> qc = q;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(qc.c[s]));
+  bf16x8 qbf[4];
+  query_operands<FMT>(qc, H, n, qbf);
 
-  // ---- QK: scores of tokens 16 nt + 4 kg + i for head n
+  // ---- QK: scores (log2 units) of tokens 16 nt + 4 kg + i for head n
   float sc[8][4];
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
-    const bool live = t0 + 16 * nt + n <= pos;       // the lane's A row (token 16 nt + n)
+    const bool live = FULL || t0 + 16 * nt + n <= pos;       // the lane's A row (token 16 nt + n)
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u32x4 a;
       if constexpr (FMT == 0) {
         uint32_t w4[4];
-        fp4x8_to_bf16(live ? r.k[nt][s] : 0u, e8m0_f32(live ? r.ks[nt] : 127u), w4);
+        fp4x8_to_bf16(live ? r.k[nt][s] : 0u, e8m0_scale(live ? r.ks[nt] : 127u), w4);
         a = u32x4{w4[0], w4[1], w4[2], w4[3]};
       } else {
         const u32x4 &src = r.k[nt][s >> 1];
-        const uint2 x = e4m3x4_to_bf16(live ? src[2 * (s & 1)] : 0u);
-        const uint2 y = e4m3x4_to_bf16(live ? src[2 * (s & 1) + 1] : 0u);
+        const uint2 x = e4m3x4_bf16(live ? src[2 * (s & 1)] : 0u);
+        const uint2 y = e4m3x4_bf16(live ? src[2 * (s & 1) + 1] : 0u);
         a = u32x4{x.x, x.y, y.x, y.y};
       }
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qbf[s], acc, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float x = acc[i] * sm_scale;
+      float x = acc[i] * qk_scale2;
       if constexpr (FMT == 1) x *= r.ks[nt][i];
-      sc[nt][i] = (t0 + 16 * nt + 4 * kg + i <= pos) ? x : NEG_INF;
+      sc[nt][i] = (FULL || t0 + 16 * nt + 4 * kg + i <= pos) ? x : NEG_INF;
     }
   }
 
-  // ---- online softmax for head n
+  // ---- online softmax for head n (base 2)
   float bm = NEG_INF;
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) bm = fmaxf(bm, sc[nt][i]);
-  bm = fmaxf(bm, __shfl_xor(bm, 16));
-  bm = fmaxf(bm, __shfl_xor(bm, 32));
-  const float m_new = fmaxf(m_run, bm);
-  const float alpha = __expf(m_run - m_new);      // 0 when m_run is -inf
+  bm = fmaxf(bm, u2f(xor_lane<16>(f2u(bm))));
+  bm = fmaxf(bm, u2f(xor_lane<32>(f2u(bm))));
+  const float m_new = FIRST ? bm : fmaxf(m_run, bm);
   float ps = 0.f;
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sc[nt][i] = __expf(sc[nt][i] - m_new);      // masked tokens: exp(-inf) = 0
+      sc[nt][i] = __builtin_amdgcn_exp2f(sc[nt][i] - m_new);      // masked tokens: 2^-inf = 0
       ps += sc[nt][i];
     }
-  l_run = l_run * alpha + ps;
-  m_run = m_new;
-  // rescale O rows (heads 4 kg + i) by their head's alpha
+  if constexpr (FIRST) {
+    l_run = ps;
+  } else {
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);     // 0 when m_run is -inf
+    l_run = l_run * alpha + ps;
+    // rescale O rows (heads 4 kg + i) by their head's alpha
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float ai = __shfl(alpha, 4 * kg + i);
+    for (int i = 0; i < 4; ++i) {
+      const float ai = __shfl(alpha, 4 * kg + i);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) O[dt][i] *= ai;
+      for (int dt = 0; dt < 8; ++dt) O[dt][i] *= ai;
+    }
   }
+  m_run = m_new;
 
   // ---- PV over 4 k-steps of 32 tokens
 #pragma unroll
@@ -202,48 +248,70 @@ __device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t
         p0 = p0 == 0.0f ? 0.0f : p0 * vs[2 * (h & 1)];
         p1 = p1 == 0.0f ? 0.0f : p1 * vs[2 * (h & 1) + 1];
       }
-      pa[h] = bf16_bits_rne(p0) | (bf16_bits_rne(p1) << 16);
+      pa[h] = bf16_pair(p0, p1);
     }
-    if constexpr (FMT == 0) {
-      uint32_t W[8][4];                           // token e, byte cb -> bf16 pair (d-tiles 2 cb, 2 cb + 1)
+    uint32_t W[8][4];                             // token e, byte pair cb -> bf16 pair (d = 8 n + 2 cb, + 1)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const bool live = t0 + pv_token(s, kg, e) <= pos;
-        const uint32_t sb = (r.vs[s][e >> 2][e & 3] >> (8 * (n >> 2))) & 0xFFu;
-        fp4x8_to_bf16(live ? r.v[s][e] : 0u, e8m0_f32(live ? sb : 127u), W[e]);
-      }
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const u32x4 blo = {lo_pair(W[0][cb], W[1][cb]), lo_pair(W[2][cb], W[3][cb]), lo_pair(W[4][cb], W[5][cb]),
-                           lo_pair(W[6][cb], W[7][cb])};
-        const u32x4 bhi = {hi_pair(W[0][cb], W[1][cb]), hi_pair(W[2][cb], W[3][cb]), hi_pair(W[4][cb], W[5][cb]),
-                           hi_pair(W[6][cb], W[7][cb])};
-        O[2 * cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
-                                                            __builtin_bit_cast(bf16x8, blo), O[2 * cb], 0, 0, 0);
-        O[2 * cb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
-                                                                __builtin_bit_cast(bf16x8, bhi), O[2 * cb + 1], 0, 0, 0);
-      }
-    } else {
-      uint32_t X0[8], X1[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const bool live = t0 + pv_token(s, kg, e) <= pos;
-        X0[e] = live ? r.v[s][e].x : 0u;
-        X1[e] = live ? r.v[s][e].y : 0u;
-      }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        u32x4 bv;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const uint32_t ca = ((dt < 4 ? X0[2 * h] : X1[2 * h]) >> (8 * (dt & 3))) & 0xFFu;
-          const uint32_t cb = ((dt < 4 ? X0[2 * h + 1] : X1[2 * h + 1]) >> (8 * (dt & 3))) & 0xFFu;
-          bv[h] = e4m3_bf16_bits(ca) | (e4m3_bf16_bits(cb) << 16);
-        }
-        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
-                                                        __builtin_bit_cast(bf16x8, bv), O[dt], 0, 0, 0);
+    for (int e = 0; e < 8; ++e) {
+      const bool live = FULL || t0 + pv_token(s, kg, e) <= pos;
+      if constexpr (FMT == 0) {
+        const uint32_t sb = __builtin_amdgcn_ubfe(r.vs[s][e >> 2][e & 3], 8 * (n >> 2), 8);
+        fp4x8_to_bf16(live ? r.v[s][e] : 0u, e8m0_scale(live ? sb : 127u), W[e]);
+      } else {
+        const uint2 x = e4m3x4_bf16(live ? r.v[s][e].x : 0u), y = e4m3x4_bf16(live ? r.v[s][e].y : 0u);
+        W[e][0] = x.x;
+        W[e][1] = x.y;
+        W[e][2] = y.x;
+        W[e][3] = y.y;
       }
     }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const u32x4 blo = {lo_pair(W[0][cb], W[1][cb]), lo_pair(W[2][cb], W[3][cb]), lo_pair(W[4][cb], W[5][cb]),
+                         lo_pair(W[6][cb], W[7][cb])};
+      const u32x4 bhi = {hi_pair(W[0][cb], W[1][cb]), hi_pair(W[2][cb], W[3][cb]), hi_pair(W[4][cb], W[5][cb]),
+                         hi_pair(W[6][cb], W[7][cb])};
+      O[2 * cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
+                                                          __builtin_bit_cast(bf16x8, blo), O[2 * cb], 0, 0, 0);
+      O[2 * cb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
+                                                              __builtin_bit_cast(bf16x8, bhi), O[2 * cb + 1], 0, 0, 0);
+    }
+  }
+}
+
+// The wave's blocks: slots slot0 + wave, + 4, ... below slot1 of a block list
+// (blk_of(slot) -> block id or -1, phys_of(blk) -> page or -1), folded into
+// the wave's softmax state. The first valid block is peeled off the loop (a
+// loop header would make the first block's page requests wait for every
+// load still in flight, the query's included), and partly masked blocks take
+// their own code path.
+template <int FMT, class BlkOf, class PhysOf>
+__device__ __forceinline__ void attend_slots(const CacheView &c, int slot0, int slot1, int pos, const QueryRegs<FMT> &q,
+                                             int H, float qk_scale2, float &m_run, float &l_run, f32x4 O[8], int n,
+                                             int kg, BlkOf blk_of, PhysOf phys_of) {
+  int slot = slot0 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  int blk = -1, phys = -1;
+  auto next = [&]() {                            // the next valid slot at or after `slot`
+    for (; slot < slot1; slot += kAttnWaves) {
+      blk = blk_of(slot);
+      if (blk < 0) continue;
+      phys = phys_of(blk);
+      if (phys >= 0) return true;
+    }
+    return false;
+  };
+  if (!next()) return;
+  if (blk * kTokens + kTokens - 1 <= pos)
+    attend_block<FMT, true, true>(c, phys, blk * kTokens, pos, q, H, qk_scale2, m_run, l_run, O, n, kg);
+  else
+    attend_block<FMT, false, true>(c, phys, blk * kTokens, pos, q, H, qk_scale2, m_run, l_run, O, n, kg);
+  slot += kAttnWaves;
+  while (next()) {
+    if (blk * kTokens + kTokens - 1 <= pos)
+      attend_block<FMT, true, false>(c, phys, blk * kTokens, pos, q, H, qk_scale2, m_run, l_run, O, n, kg);
+    else
+      attend_block<FMT, false, false>(c, phys, blk * kTokens, pos, q, H, qk_scale2, m_run, l_run, O, n, kg);
+    slot += kAttnWaves;
   }
 }
 
@@ -257,8 +325,9 @@ __device__ __forceinline__ void put(float *p, float v) {
     *p = v;
 }
 
-// This wave's sums for head n, then the 4-wave merge through LDS into the
-// workgroup's partial (m, l, O) of partition p.
+// This wave's sums for head n (m_run in log2 units), then the 4-wave merge
+// through LDS into the workgroup's partial (m, l, O) of partition p; m is
+// stored in natural-log units.
 template <bool COHERENT>
 __device__ __forceinline__ void write_partial(float (&s_m)[kAttnWaves][16], float (&s_l)[kAttnWaves][16],
                                               float (&s_o)[kAttnWaves][16][kDim + 4], float m_run, float l_run,
@@ -267,8 +336,8 @@ __device__ __forceinline__ void write_partial(float (&s_m)[kAttnWaves][16], floa
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, kg = lane >> 4;
   const float NEG_INF = -__builtin_inff();
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run += u2f(xor_lane<16>(f2u(l_run)));
+  l_run += u2f(xor_lane<32>(f2u(l_run)));
   if (kg == 0) {
     s_m[wave][n] = m_run;
     s_l[wave][n] = l_run;
@@ -281,21 +350,28 @@ __device__ __forceinline__ void write_partial(float (&s_m)[kAttnWaves][16], floa
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, s_m[w][h]);
     const float mine = s_m[wave][h];
-    const float f = (mine == NEG_INF) ? 0.0f : __expf(mine - M);
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) s_o[wave][h][8 * n + dt] = O[dt][i] * f;
+    const float f = (mine == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(mine - M);
+    f32x4 *dst = reinterpret_cast<f32x4 *>(&s_o[wave][h][8 * n]);
+    dst[0] = f32x4{O[0][i] * f, O[1][i] * f, O[2][i] * f, O[3][i] * f};
+    dst[1] = f32x4{O[4][i] * f, O[5][i] * f, O[6][i] * f, O[7][i] * f};
   }
   lds_barrier();
   const int64_t part = (int64_t)row * H;      // + h, then * P + p
+  float *const row_o = sp_o + part * P * kDim;
+  const __amdgpu_buffer_rsrc_t ro = row_rsrc(row_o, H * P * kDim);
 #pragma unroll
-  for (int rr = 0; rr < 8; ++rr) {
+  for (int rr = 0; rr < 2; ++rr) {
     const int idx = threadIdx.x + 256 * rr;
-    const int h = idx >> 7, d = idx & 127;
+    const int h = idx >> 5, d = 4 * (idx & 31);
     if (h < H) {
-      float o = 0.f;
+      f32x4 o = *reinterpret_cast<const f32x4 *>(&s_o[0][h][d]);
 #pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) o += s_o[w][h][d];
-      put<COHERENT>(sp_o + ((part + h) * P + p) * kDim + d, o);
+      for (int w = 1; w < kAttnWaves; ++w) o += *reinterpret_cast<const f32x4 *>(&s_o[w][h][d]);
+      const int32_t off = (h * P + p) * kDim + d;
+      if constexpr (COHERENT)
+        store4_coherent(ro, off, o);
+      else
+        *reinterpret_cast<f32x4 *>(row_o + off) = o;
     }
   }
   if (threadIdx.x < (unsigned)H) {
@@ -306,8 +382,8 @@ __device__ __forceinline__ void write_partial(float (&s_m)[kAttnWaves][16], floa
     float Lsum = 0.f;
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w)
-      Lsum += (s_m[w][h] == NEG_INF) ? 0.0f : s_l[w][h] * __expf(s_m[w][h] - M);
-    put<COHERENT>(sp_m + (part + h) * P + p, M);
+      Lsum += (s_m[w][h] == NEG_INF) ? 0.0f : s_l[w][h] * __builtin_amdgcn_exp2f(s_m[w][h] - M);
+    put<COHERENT>(sp_m + (part + h) * P + p, M * kLn2);
     put<COHERENT>(sp_l + (part + h) * P + p, Lsum);
   }
 }
@@ -327,20 +403,23 @@ __global__ __launch_bounds__(256) void k_split_attn(CacheView c, const void *__r
   const int pos = c.context_lens[b] - q_rows + j;
   const int cps = (topk + P - 1) / P;
   const int slot0 = p * cps, slot1 = min(slot0 + cps, (int)topk);
-  bf16x8 qbf[4];
-  load_query<FMT>(qv, row, H, n, kg, qbf);
+  QueryRegs<FMT> qr;
+  load_query<FMT>(qv, row, H, n, kg, qr);
 
   float m_run = -__builtin_inff(), l_run = 0.0f;
   f32x4 O[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int slot = slot0 + wave; slot < slot1; slot += kAttnWaves) {
-    const int blk = block_table[(int64_t)row * topk + slot];
-    if (blk < 0 || blk >= c.stride || blk * kTokens > pos) continue;
-    const int phys = c.page_table[(int64_t)b * c.stride + blk];
-    if (phys < 0 || phys >= c.num_pages) continue;
-    attend_block<FMT>(c, phys, blk * kTokens, pos, qbf, sm_scale, m_run, l_run, O, n, kg);
-  }
+  attend_slots<FMT>(
+      c, slot0, slot1, pos, qr, H, sm_scale * kLog2e, m_run, l_run, O, n, kg,
+      [&](int slot) {
+        const int blk = __builtin_amdgcn_readfirstlane(block_table[(int64_t)row * topk + slot]);
+        return (blk < 0 || blk >= c.stride || blk * kTokens > pos) ? -1 : blk;
+      },
+      [&](int blk) {
+        const int phys = __builtin_amdgcn_readfirstlane(c.page_table[(int64_t)b * c.stride + blk]);
+        return (phys < 0 || phys >= c.num_pages) ? -1 : phys;
+      });
   write_partial<false>(s_m, s_l, s_o, m_run, l_run, O, row, H, P, p, sp_m, sp_l, sp_o);
 }
 
@@ -390,18 +469,19 @@ __global__ __launch_bounds__(256) void k_select_attn(CacheView c, const float *_
 
   const int cps = (topk + P - 1) / P;
   const int slot0 = p * cps, slot1 = min(slot0 + cps, n_sel);
-  bf16x8 qbf[4];                                   // requested with the first block's pages
-  load_query<FMT>(qv, row, H, n, kg, qbf);
+  QueryRegs<FMT> qr;                               // widened after the first block's pages are requested
+  load_query<FMT>(qv, row, H, n, kg, qr);
   float m_run = -__builtin_inff(), l_run = 0.0f;
   f32x4 O[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int slot = slot0 + wave; slot < slot1; slot += kAttnWaves) {
-    const int blk = __builtin_amdgcn_readlane((int)sel, slot);      // a candidate: blk * 128 <= pos
-    const int phys = s_pt[blk];
-    if (phys < 0 || phys >= c.num_pages) continue;
-    attend_block<FMT>(c, phys, blk * kTokens, pos, qbf, sm_scale, m_run, l_run, O, n, kg);
-  }
+  attend_slots<FMT>(
+      c, slot0, slot1, pos, qr, H, sm_scale * kLog2e, m_run, l_run, O, n, kg,
+      [&](int slot) { return __builtin_amdgcn_readlane((int)sel, slot); },   // a candidate: blk * 128 <= pos
+      [&](int blk) {
+        const int phys = __builtin_amdgcn_readfirstlane(s_pt[blk]);
+        return (phys < 0 || phys >= c.num_pages) ? -1 : phys;
+      });
   write_partial<true>(s_m, s_l, s_o, m_run, l_run, O, row, H, P, p, sp_m, sp_l, sp_o);
 
   // ---- the row's merge, by its last partition workgroup to finish. The

@@ -30,6 +30,21 @@ __device__ __forceinline__ float2 get2(const float2 *p) {
   }
 }
 
+// Device-coherent 16-byte partial traffic for the decode step's in-launch
+// merge: buffer loads / stores with the sc1 cache-policy bit (the bit an
+// agent-scope relaxed atomic load or store carries), through a descriptor
+// over one query row's partials (bounds-checked by the hardware).
+constexpr int kCoherentBits = 16;                     // sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float *base, int32_t n_floats) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, n_floats * 4, 0x00020000);
+}
+__device__ __forceinline__ f32x4 load4_coherent(__amdgpu_buffer_rsrc_t rs, int32_t float_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rs, float_off * 4, 0, kCoherentBits);
+}
+__device__ __forceinline__ void store4_coherent(__amdgpu_buffer_rsrc_t rs, int32_t float_off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, float_off * 4, 0, kCoherentBits);
+}
+
 template <bool COHERENT = false>
 __device__ __forceinline__ void merge_one(const float *__restrict__ sp_m, const float *__restrict__ sp_l,
                                           const float *__restrict__ sp_o, int64_t r, int32_t P, int lane,
@@ -94,17 +109,44 @@ __device__ __forceinline__ void merge_row(const float *__restrict__ sp_m, const 
   float M = NEG_INF, Lsum = 0.f, acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  const __amdgpu_buffer_rsrc_t ro = row_rsrc(sp_o + row * H * P * kDim, H * P * kDim);
+  // (m, l) of 4 partitions per 16-byte load when P is a multiple of 4 (the
+  // row's (m, l) arrays are then 16-byte aligned); reads past the row's last
+  // head return 0 (descriptor bound) and, like every u >= P - p0, weigh nothing
+  const bool ml4 = (P & 3) == 0;
+  const __amdgpu_buffer_rsrc_t rm = row_rsrc(sp_m + row * H * P, H * P), rl = row_rsrc(sp_l + row * H * P, H * P);
   for (int p0 = 0; p0 < P; p0 += 8) {
     float m[8], l[8];
-    float2 o[8][4];
+    f32x4 o[8][2];
+    if (COHERENT && ml4) {
+      const f32x4 m0 = load4_coherent(rm, h * P + p0), m1 = load4_coherent(rm, h * P + p0 + 4);
+      const f32x4 l0 = load4_coherent(rl, h * P + p0), l1 = load4_coherent(rl, h * P + p0 + 4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        m[u] = m0[u];
+        m[u + 4] = m1[u];
+        l[u] = l0[u];
+        l[u + 4] = l1[u];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {               // clamped, unconditional
+        const int pp = min(p0 + u, P - 1);
+        m[u] = get<COHERENT>(sp_m + r * P + pp);
+        l[u] = get<COHERENT>(sp_l + r * P + pp);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {                 // clamped, unconditional; u >= P - p0 weigh nothing
       const int pp = min(p0 + u, P - 1);
-      m[u] = get<COHERENT>(sp_m + r * P + pp);
-      l[u] = get<COHERENT>(sp_l + r * P + pp);
-      const float2 *po = reinterpret_cast<const float2 *>(sp_o + (r * P + pp) * kDim + e0);
+      const int32_t off = (h * P + pp) * kDim + e0;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) o[u][k] = get2<COHERENT>(po + k);
+      for (int k = 0; k < 2; ++k) {
+        if constexpr (COHERENT)
+          o[u][k] = load4_coherent(ro, off + 4 * k);
+        else
+          o[u][k] = *reinterpret_cast<const f32x4 *>(sp_o + row * H * P * kDim + off + 4 * k);
+      }
     }
     float Mc = M;
 #pragma unroll
@@ -119,26 +161,25 @@ __device__ __forceinline__ void merge_row(const float *__restrict__ sp_m, const 
       if (wu != 0.0f) {
         Lsum += l[u] * wu;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          acc[2 * k] += wu * o[u][k].x;
-          acc[2 * k + 1] += wu * o[u][k].y;
-        }
+        for (int e = 0; e < 8; ++e) acc[e] += wu * o[u][e >> 2][e & 3];
       }
     }
     M = Mc;
   }
   const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
-  uint32_t packed[4];
+  u32x4 packed;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t u0 = f2u(acc[2 * k] * inv), u1 = f2u(acc[2 * k + 1] * inv);
-    const uint32_t b0 = (u0 + 0x7FFFu + ((u0 >> 16) & 1u)) >> 16;   // round to nearest even
-    const uint32_t b1 = (u1 + 0x7FFFu + ((u1 >> 16) & 1u)) >> 16;
-    packed[k] = b0 | (b1 << 16);
+  for (int k = 0; k < 4; ++k) {                   // round to nearest even (v_cvt_pk_bf16_f32)
+    const bf16x2 v = {(__bf16)(acc[2 * k] * inv), (__bf16)(acc[2 * k + 1] * inv)};
+    packed[k] = bf16x2_bits(v);
   }
-  uint32_t *dst = reinterpret_cast<uint32_t *>(out + r * kDim + e0);   // out: 4-byte aligned
+  uint16_t *const dst = out + r * kDim + e0;      // out: at least 4-byte aligned
+  if ((reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+    *reinterpret_cast<u32x4 *>(dst) = packed;
+  } else {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) dst[k] = packed[k];
+    for (int k = 0; k < 4; ++k) reinterpret_cast<uint32_t *>(dst)[k] = packed[k];
+  }
   if (lse && (t & 15) == 0) lse[r] = Lsum > 0.0f ? M + __logf(Lsum) : NEG_INF;
 }
 
