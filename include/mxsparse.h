@@ -223,6 +223,25 @@ int decode_step(const mxs_step *step, void *ws, size_t ws_bytes, void *stream);
 size_t mxs_workspace_bytes(int32_t B, int32_t q, int32_t H, int32_t H_I, int32_t topk,
                            int32_t page_table_stride, int32_t num_partitions);
 
+/* decode_step_reuse: the step of a layer that reuses an earlier layer's sparse
+ * block selection instead of making its own (ATOM PR #2686, "Enable Mono
+ * decode with fixed DSpark verify": under an index_topk_freq schedule some
+ * sparse layers reuse a selection; the first layer still selects its own).
+ * Stages 1, 2, 5 and 6 on one stream, as two launches: the step's new K and
+ * V rows into the pages and the query as e4m3 (MXFP4 KV), then split
+ * attention over the given blocks and the merge. Nothing of the index side
+ * is read or written: step->idx_new, q_idx, w, H_I, block_table_out and
+ * scores_out and cache.idx_pages are ignored; k_new and v_new are given both
+ * or neither.
+ *   block_table  [B][q][topk] int32: the reused selection (as topk_blocks
+ *                writes it: ascending, -1 padded); entries < 0, >= the page
+ *                table stride or past the row's position are skipped
+ *   ws           as for decode_step (mxs_workspace_bytes, 256 B aligned,
+ *                scratch; calls in flight at once must not share one)
+ * Errors as for decode_step; MXS_EINVAL when block_table is null. */
+int decode_step_reuse(const mxs_step *step, const int32_t *block_table, void *ws, size_t ws_bytes,
+                      void *stream);
+
 /* ---- diagnostics ---------------------------------------------------------- */
 const char *mxs_status_str(int status);
 const char *mxs_last_error(void);

@@ -106,3 +106,48 @@ def decode_step_ref(inp, pools=None, seqs=None) -> dict:
             O[b, j], lse[b, j] = attention.sparse_attention_row(
                 q_att[b, j], K_all, V_all, table[b, j], int(pos[j]), wl.sm_scale)
     return {"pools": pools, "q8": q8, "scores": scores, "block_table": table, "O": O, "lse": lse}
+
+
+def decode_step_reuse_ref(inp, block_table: np.ndarray, pools=None, seqs=None) -> dict:
+    """The step of a layer that reuses an earlier layer's sparse block selection
+    (ATOM PR #2686, "Enable Mono decode with fixed DSpark verify", the review
+    thread's commit message: under an index_topk_freq schedule a layer can
+    reuse a selection instead of making its own).
+
+    Reading: such a layer scores nothing, so the step is the row store of its
+    new K and V rows, the query store and attention of each row over the given
+    blocks [B][q][k] (entries < 0 or past the row's position contribute no
+    tokens), then the merge. The index pool is neither read nor written.
+    Returns the post-step pools ("k", "v"), the query codes and O, lse as
+    ``decode_step_ref`` does."""
+    wl = inp.wl
+    seqs = list(range(wl.B)) if seqs is None else list(seqs)
+    fmts = {"k": wl.kv_format, "v": wl.kv_format}
+    if pools is None:
+        pools = {s: build_cache(inp, s, fmts[s], seqs) for s in fmts}
+    pools = {s: pools[s].copy() for s in fmts}
+    if wl.full_step:
+        for s, f in fmts.items():
+            for b in seqs:
+                L = int(inp.contexts[b])
+                formats.STORE[f](pools[s], inp.page_table[b], L - wl.q, inp.rows(s, b)[L - wl.q:])
+    q_att, q8 = attention_query(inp)
+    B, q, H = wl.B, wl.q, wl.H
+    O = np.full((B, q, H, 128), np.nan)
+    lse = np.full((B, q, H), np.nan)
+    for b in seqs:
+        L = int(inp.contexts[b])
+        pos = indexer.row_positions(L, q)
+        ids = np.asarray(block_table[b])
+        sel = np.unique(ids[(ids >= 0) & (ids * TOKENS < L)])
+        toks = (np.concatenate([np.arange(i * TOKENS, min((i + 1) * TOKENS, L)) for i in sel])
+                if len(sel) else np.zeros(0, dtype=np.int64))
+        K_all = np.zeros((L, 128))
+        V_all = np.zeros((L, 128))
+        if len(toks):
+            K_all[toks] = formats.READ[wl.kv_format](pools["k"], inp.page_table[b], L, toks)
+            V_all[toks] = formats.READ[wl.kv_format](pools["v"], inp.page_table[b], L, toks)
+        for j in range(q):
+            O[b, j], lse[b, j] = attention.sparse_attention_row(
+                q_att[b, j], K_all, V_all, ids[j], int(pos[j]), wl.sm_scale)
+    return {"pools": pools, "q8": q8, "O": O, "lse": lse}

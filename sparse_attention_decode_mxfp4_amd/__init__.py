@@ -24,7 +24,7 @@ PAGE_BYTES = {"mxfp4": 8704, "fp8": 16896}
 EXPORTS = [
     "mxfp4_row_store", "fp8_row_store", "pack_q_e4m3", "index_score", "topk_blocks",
     "index_score_topk", "mxs_score_workspace_bytes", "sparse_split_attn", "mxs_default_partitions",
-    "lse_merge", "decode_step", "mxs_workspace_bytes", "mxs_status_str", "mxs_last_error",
+    "lse_merge", "decode_step", "decode_step_reuse", "mxs_workspace_bytes", "mxs_status_str", "mxs_last_error",
     "mxs_abi_version",
 ]
 
@@ -79,6 +79,7 @@ def lib() -> ctypes.CDLL:
             "sparse_split_attn": [P, P, I32, P, I32, I32, I32, I32, I32, F32, P, P, P, P],
             "lse_merge": [P, P, P, I32, I32, P, P, P],
             "decode_step": [P, P, SZ, P],
+            "decode_step_reuse": [P, P, P, SZ, P],
             "mxs_default_partitions": [I32, I32, I32],
             "mxs_score_workspace_bytes": [I32, I32, I32],
             "mxs_workspace_bytes": [I32, I32, I32, I32, I32, I32, I32],
@@ -320,4 +321,46 @@ class DecodeStep:
     def run(self, stream=None):
         s = _stream() if stream is None else stream
         _check(lib().decode_step(ctypes.byref(self.struct), self._ws_ptr, self.ws.numel(), s))
+        return self.out
+
+
+class DecodeStepReuse:
+    """decode_step_reuse over fixed tensors: the step of a layer that reuses an
+    earlier layer's block selection (``block_table`` [B][q][topk] int32). Stores
+    the new K / V rows (both or neither), packs the query and attends over the
+    given blocks; the index side is not touched. ``run()`` is a single C call."""
+
+    def __init__(self, cache: Cache, query, block_table, sm_scale, k_new=None, v_new=None, num_partitions=0,
+                 out=None, lse=None, ws=None):
+        B, q, H, _ = query.shape
+        cache.check_batch(B)
+        topk = block_table.shape[-1]
+        dev = query.device
+        if query.dtype == torch.float32:
+            qd = MXS_F32
+        elif query.dtype == torch.bfloat16:
+            qd = MXS_BF16
+        else:
+            raise TypeError("query: fp32 or bf16")
+        self.out = out if out is not None else torch.empty((B, q, H, 128), dtype=torch.bfloat16, device=dev)
+        self.lse = lse if lse is not None else torch.empty((B, q, H), dtype=torch.float32, device=dev)
+        nb = workspace_bytes(B, q, H, 1, topk, cache.stride, num_partitions)
+        self.ws = ws if ws is not None else torch.empty(nb, dtype=torch.uint8, device=dev)
+        if self.ws.numel() < nb:
+            raise ValueError(f"ws: {self.ws.numel()} bytes, needs {nb}")
+        self.cache = cache
+        self._keep = (query, block_table, k_new, v_new)
+        self._table = _dev(block_table, torch.int32, "block_table", (B, q, topk))
+        self.struct = StepStruct(
+            cache.struct,
+            _opt(k_new, torch.float32, "k_new", (B, q, 128)), _opt(v_new, torch.float32, "v_new", (B, q, 128)),
+            None, _dev(query, query.dtype, "query"), qd, None, None,
+            B, q, H, 0, topk, num_partitions, float(sm_scale),
+            _dev(self.out, torch.bfloat16, "out", (B, q, H, 128)), _opt(self.lse, torch.float32, "lse", (B, q, H)),
+            None, None)
+        self._ws_ptr = _dev(self.ws, torch.uint8, "ws")
+
+    def run(self, stream=None):
+        s = _stream() if stream is None else stream
+        _check(lib().decode_step_reuse(ctypes.byref(self.struct), self._table, self._ws_ptr, self.ws.numel(), s))
         return self.out

@@ -368,4 +368,61 @@ int decode_step(const mxs_step *a, void *ws, size_t ws_bytes, void *stream) {
                   "decode_step: top-k + split attention + merge");
 }
 
+int decode_step_reuse(const mxs_step *a, const int32_t *block_table, void *ws, size_t ws_bytes, void *stream) {
+  REQ(a, MXS_EINVAL, "step: null");
+  const mxs_cache *cache = &a->cache;
+  if (int r = check_cache(cache, false, true)) return r;
+  if (int r = check_rows(a->B, a->q)) return r;
+  if (int r = check_topk(a->topk)) return r;
+  if (a->B == 0) return ok();                      // an empty batch: nothing to do
+  const int32_t P = a->num_partitions == 0 ? default_partitions(a->topk) : a->num_partitions;
+  const bool mx = cache->kv_format == MXS_FMT_MXFP4;
+  if (mx)
+    REQ(a->q_dtype == MXS_F32 || a->q_dtype == MXS_BF16, MXS_EUNSUPPORTED,
+        "q_dtype: %d; an MXFP4 KV step takes an fp32 or bf16 query and stores it as e4m3", a->q_dtype);
+  else
+    REQ(a->q_dtype == MXS_BF16, MXS_EUNSUPPORTED, "q_dtype: %d; an FP8 KV step takes a bf16 query", a->q_dtype);
+  REQ(a->query && aligned(a->query, 16), MXS_EINVAL, "query: null or not 16-byte aligned");
+  REQ(!a->k_new == !a->v_new, MXS_EINVAL, "k_new / v_new: give both or neither");
+  REQ((!a->k_new || aligned(a->k_new, 8)) && (!a->v_new || aligned(a->v_new, 8)), MXS_EINVAL,
+      "k_new / v_new: not 8-byte aligned");
+  REQ(block_table && aligned(block_table, 4), MXS_EINVAL, "block_table: null or misaligned");
+  REQ(a->H >= 1, MXS_EINVAL, "H: %d, must be >= 1", a->H);
+  REQ(a->H <= MXS_MAX_H, MXS_EUNSUPPORTED, "H: %d query heads per KV head, more than %d", a->H, MXS_MAX_H);
+  REQ(P >= 1 && P <= MXS_MAX_PARTITIONS, MXS_EUNSUPPORTED, "num_partitions: %d, must be in 1..%d", P,
+      MXS_MAX_PARTITIONS);
+  REQ(std::isfinite(a->sm_scale), MXS_EINVAL, "sm_scale: not finite");
+  REQ(a->out && aligned(a->out, 4), MXS_EINVAL, "out: null or misaligned");
+  REQ(!a->lse || aligned(a->lse, 4), MXS_EINVAL, "lse: misaligned");
+  const StepWs w = step_ws(a->B, a->q, a->H, a->topk, cache->page_table_stride, P);
+  REQ(ws, MXS_EWORKSPACE, "decode_step_reuse: workspace null (needs %zu bytes)", w.total);
+  REQ(ws_bytes >= w.total, MXS_EWORKSPACE, "decode_step_reuse: workspace %zu bytes, needs %zu", ws_bytes, w.total);
+  REQ(aligned(ws, 256), MXS_EINVAL, "ws: not 256-byte aligned");
+
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  uint8_t *q8 = base + w.q8;
+  float *sp_m = reinterpret_cast<float *>(base + w.sp_m);
+  float *sp_l = reinterpret_cast<float *>(base + w.sp_l);
+  float *sp_o = reinterpret_cast<float *>(base + w.sp_o);
+  uint32_t *counters = reinterpret_cast<uint32_t *>(base + w.counters);
+  const hipStream_t s = (hipStream_t)stream;
+  const mxs::CacheView c = view(cache);
+
+  // 1 - 2: the new K / V rows into the pages, q -> e4m3 (MXFP4 KV) and the
+  // merge counters cleared, one launch
+  if (int r = launched(mxs::launch_reuse_store(c, a->k_new, a->v_new, a->query, a->q_dtype, a->H, mx ? q8 : nullptr,
+                                               counters, a->B, a->q, s),
+                       "decode_step_reuse: store"))
+    return r;
+  // 5 - 6: split attention over the given blocks and the merge, one launch
+  const void *qa = mx ? static_cast<const void *>(q8) : a->query;
+  mxs::FusedMerge fm;
+  fm.counters = counters;
+  fm.out = a->out;
+  fm.lse = a->lse;
+  return launched(mxs::launch_table_attn(c, block_table, qa, a->B, a->q, a->H, a->topk, P, a->sm_scale, sp_m, sp_l,
+                                         sp_o, fm, s),
+                  "decode_step_reuse: split attention + merge");
+}
+
 }  // extern "C"

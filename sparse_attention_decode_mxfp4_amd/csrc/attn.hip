@@ -423,49 +423,60 @@ __global__ __launch_bounds__(256) void k_split_attn(CacheView c, const void *__r
   write_partial<false>(s_m, s_l, s_o, m_run, l_run, O, row, H, P, p, sp_m, sp_l, sp_o);
 }
 
-// The decode step's attention: the workgroup first selects its row's top-k
-// blocks itself (the workgroup selection of topk.hpp over the row's scores),
-// with the row's page table staged in LDS, then attends to the slots of its
-// partition. Everything it needs from memory before the K / V pages — the
-// context length, the score row and the page-table row — is requested in one
-// round trip; the query goes out with the first block's pages. Partition 0
-// also writes the row's block table.
-template <int FMT, int ITEMS>
+// The decode step's attention. SELECT: the workgroup first selects its row's
+// top-k blocks itself (the workgroup selection of topk.hpp over the row's
+// scores) and partition 0 writes the row's block table; otherwise the row's
+// blocks come from a given block table (a selection reused from an earlier
+// layer; entries < 0, past the table or past the row's position are
+// skipped). The row's page table is staged in LDS. Everything the workgroup
+// needs from memory before the K / V pages — the context length, the score
+// row or table row and the page-table row — is requested in one round trip;
+// the query goes out with the first block's pages.
+template <int FMT, int ITEMS, bool SELECT>
 __global__ __launch_bounds__(256) void k_select_attn(CacheView c, const float *__restrict__ scores,
                                                      const void *__restrict__ qv, int32_t q_rows, int32_t H,
                                                      int32_t topk, int32_t P, float sm_scale,
                                                      int32_t *__restrict__ block_table, float *__restrict__ sp_m,
                                                      float *__restrict__ sp_l, float *__restrict__ sp_o,
                                                      FusedMerge fm) {
-  __shared__ TopkSmem<ITEMS> tk;
+  __shared__ TopkSmem<SELECT ? ITEMS : 1> tk;
   __shared__ int32_t s_pt[kTopkThreads * ITEMS];
   __shared__ float s_m[kAttnWaves][16], s_l[kAttnWaves][16];
   __shared__ float s_o[kAttnWaves][16][kDim + 4];
   __shared__ uint32_t s_last;
   const int p = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int row = b * q_rows + j;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int n = lane & 15, kg = lane >> 4;
   const int stride = c.stride;
 
   const int L = c.context_lens[b];
   float v[ITEMS];
   int32_t pt[ITEMS];
+  int32_t given = -1;
 #pragma unroll
   for (int r = 0; r < ITEMS; ++r) {
     const int i = min(tid + kTopkThreads * r, stride - 1);   // clamped: unconditional loads
-    v[r] = scores[(int64_t)row * stride + i];
+    if constexpr (SELECT) v[r] = scores[(int64_t)row * stride + i];
     pt[r] = c.page_table[(int64_t)b * stride + i];
   }
+  if constexpr (!SELECT) given = block_table[(int64_t)row * topk + min(lane, topk - 1)];
   const int pos = L - q_rows + j;
-  const int n_cand = pos < 0 ? 0 : min(pos / kTokens + 1, stride);
 #pragma unroll
   for (int r = 0; r < ITEMS; ++r)
     if (tid + kTopkThreads * r < stride) s_pt[tid + kTopkThreads * r] = pt[r];
   int n_sel;
-  const uint32_t sel = wg_topk<ITEMS>(v, n_cand, topk, tk, n_sel);
-  lds_barrier();                                   // s_pt (the selection may return before any barrier)
-  if (p == 0 && tid < topk) block_table[(int64_t)row * topk + tid] = tid < n_sel ? (int32_t)sel : -1;
+  uint32_t sel;
+  if constexpr (SELECT) {
+    const int n_cand = pos < 0 ? 0 : min(pos / kTokens + 1, stride);
+    sel = wg_topk<ITEMS>(v, n_cand, topk, tk, n_sel);
+    lds_barrier();                                 // s_pt (the selection may return before any barrier)
+    if (p == 0 && tid < topk) block_table[(int64_t)row * topk + tid] = tid < n_sel ? (int32_t)sel : -1;
+  } else {
+    sel = (uint32_t)given;                         // lane s: slot s (lanes >= topk are never read)
+    n_sel = topk;
+    lds_barrier();                                 // s_pt
+  }
 
   const int cps = (topk + P - 1) / P;
   const int slot0 = p * cps, slot1 = min(slot0 + cps, n_sel);
@@ -477,7 +488,11 @@ __global__ __launch_bounds__(256) void k_select_attn(CacheView c, const float *_
   for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   attend_slots<FMT>(
       c, slot0, slot1, pos, qr, H, sm_scale * kLog2e, m_run, l_run, O, n, kg,
-      [&](int slot) { return __builtin_amdgcn_readlane((int)sel, slot); },   // a candidate: blk * 128 <= pos
+      [&](int slot) {
+        const int blk = __builtin_amdgcn_readlane((int)sel, slot);
+        if constexpr (SELECT) return blk;          // a candidate: 0 <= blk, blk * 128 <= pos
+        return (blk < 0 || blk >= stride || blk * kTokens > pos) ? -1 : blk;
+      },
       [&](int blk) {
         const int phys = __builtin_amdgcn_readfirstlane(s_pt[blk]);
         return (phys < 0 || phys >= c.num_pages) ? -1 : phys;
@@ -515,14 +530,14 @@ hipError_t launch_split_attn(const CacheView &c, const void *q, int q_dtype, con
   return hipGetLastError();
 }
 
-hipError_t launch_select_attn(const CacheView &c, const float *scores, const void *q, int32_t B, int32_t q_rows,
+template <bool SELECT>
+static void launch_attn_items(const CacheView &c, const float *scores, const void *q, int32_t B, int32_t q_rows,
                               int32_t H, int32_t topk, int32_t P, float sm_scale, int32_t *block_table, float *sp_m,
                               float *sp_l, float *sp_o, const FusedMerge &fm, hipStream_t s) {
-  if (B * q_rows == 0) return hipSuccess;
   const dim3 grid((unsigned)P, (unsigned)q_rows, (unsigned)B), block(kTopkThreads);
 #define MXS_SELECT_ATTN(F, I)                                                                                   \
-  hipLaunchKernelGGL((k_select_attn<F, I>), grid, block, 0, s, c, scores, q, q_rows, H, topk, P, sm_scale,     \
-                     block_table, sp_m, sp_l, sp_o, fm)
+  hipLaunchKernelGGL((k_select_attn<F, I, SELECT>), grid, block, 0, s, c, scores, q, q_rows, H, topk, P,       \
+                     sm_scale, block_table, sp_m, sp_l, sp_o, fm)
   if (c.kv_format == 0) {
     if (c.stride <= kTopkThreads * 2) MXS_SELECT_ATTN(0, 2);
     else if (c.stride <= kTopkThreads * 8) MXS_SELECT_ATTN(0, 8);
@@ -533,6 +548,22 @@ hipError_t launch_select_attn(const CacheView &c, const float *scores, const voi
     else MXS_SELECT_ATTN(1, 32);
   }
 #undef MXS_SELECT_ATTN
+}
+
+hipError_t launch_select_attn(const CacheView &c, const float *scores, const void *q, int32_t B, int32_t q_rows,
+                              int32_t H, int32_t topk, int32_t P, float sm_scale, int32_t *block_table, float *sp_m,
+                              float *sp_l, float *sp_o, const FusedMerge &fm, hipStream_t s) {
+  if (B * q_rows == 0) return hipSuccess;
+  launch_attn_items<true>(c, scores, q, B, q_rows, H, topk, P, sm_scale, block_table, sp_m, sp_l, sp_o, fm, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_table_attn(const CacheView &c, const int32_t *block_table, const void *q, int32_t B, int32_t q_rows,
+                             int32_t H, int32_t topk, int32_t P, float sm_scale, float *sp_m, float *sp_l, float *sp_o,
+                             const FusedMerge &fm, hipStream_t s) {
+  if (B * q_rows == 0) return hipSuccess;
+  launch_attn_items<false>(c, nullptr, q, B, q_rows, H, topk, P, sm_scale, const_cast<int32_t *>(block_table), sp_m,
+                           sp_l, sp_o, fm, s);
   return hipGetLastError();
 }
 

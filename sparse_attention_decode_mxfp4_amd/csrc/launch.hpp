@@ -19,6 +19,11 @@ struct CacheView {
 hipError_t launch_row_store(int format, const float *rows, int64_t n, const int64_t *slots,
                             uint8_t *pages, int32_t num_pages, hipStream_t s);
 hipError_t launch_pack_q(const void *q, int q_dtype, int64_t n, uint8_t *q8, hipStream_t s);
+// the stores of a step that reuses a block selection: the new K / V rows of
+// [B][q][128] fp32 (row j of sequence b at position L_b - q + j; either null:
+// none), the query packed to e4m3 when q8 is non-null, counters [B][q] cleared
+hipError_t launch_reuse_store(const CacheView &c, const float *k_new, const float *v_new, const void *q, int q_dtype,
+                              int32_t H, uint8_t *q8, uint32_t *counters, int32_t B, int32_t q_rows, hipStream_t s);
 
 // The decode step's own stores, done inside the scorer launch (all null: none):
 // the new K / V / index rows [B][q][128] fp32 (row j of sequence b goes to
@@ -58,6 +63,11 @@ struct FusedMerge {
 hipError_t launch_select_attn(const CacheView &c, const float *scores, const void *q, int32_t B, int32_t q_rows,
                               int32_t H, int32_t topk, int32_t P, float sm_scale, int32_t *block_table, float *sp_m,
                               float *sp_l, float *sp_o, const FusedMerge &fm, hipStream_t s);
+// the same launch over a given block table [B][q_rows][topk] (a reused
+// selection: entries < 0, past the table or past the row's position are skipped)
+hipError_t launch_table_attn(const CacheView &c, const int32_t *block_table, const void *q, int32_t B, int32_t q_rows,
+                             int32_t H, int32_t topk, int32_t P, float sm_scale, float *sp_m, float *sp_l, float *sp_o,
+                             const FusedMerge &fm, hipStream_t s);
 
 // merge (merge.hip)
 hipError_t launch_lse_merge(const float *sp_m, const float *sp_l, const float *sp_o, int32_t n_rows,

@@ -1,5 +1,6 @@
-// Row store and q store as stand-alone launches (the decode step does both
-// inside its scorer launch).
+// Row store and q store as stand-alone launches, and the store launch of a
+// step that reuses an earlier layer's block selection (the full decode step
+// does its stores inside its scorer launch).
 //
 // ATOM PR #2812, "Mono decode over the MXFP4 KV and index caches": the
 // MXFP4 index-cache commit writes each index-key row into an 8704 B page
@@ -38,6 +39,46 @@ __global__ __launch_bounds__(256) void k_row_store(const float *__restrict__ row
 __global__ __launch_bounds__(256) void k_pack_q(const void *__restrict__ q, int q_dtype, int64_t n,
                                                 uint8_t *__restrict__ q8) {
   pack_q4(q, q_dtype, n, q8, ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4);
+}
+
+// The stores of a step that reuses an earlier layer's block selection (the
+// pages' index_topk_freq schedule: such a layer scores nothing). Workgroup
+// (b, j) stores the new K and V rows of position L_b - q + j (wave 0: K,
+// wave 1: V; skipped when that position has no valid page), packs the row's
+// H x 128 query elements to e4m3 (waves 2 - 3, when q8 is given) and clears
+// the row's merge counter for the attention launch that follows.
+__global__ __launch_bounds__(256) void k_reuse_store(CacheView c, const float *__restrict__ k_new,
+                                                     const float *__restrict__ v_new, const void *__restrict__ q,
+                                                     int q_dtype, int H, uint8_t *__restrict__ q8,
+                                                     uint32_t *__restrict__ counters, int q_rows) {
+  const int row = blockIdx.x, b = row / q_rows, j = row % q_rows;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (tid == 0) counters[row] = 0u;
+  if (wave < 2) {
+    const float *src = wave == 0 ? k_new : v_new;
+    if (!src) return;
+    const int pos = c.context_lens[b] - q_rows + j;
+    if (pos < 0 || pos / kTokens >= c.stride) return;
+    const int phys = c.page_table[(int64_t)b * c.stride + pos / kTokens];
+    if (phys < 0 || phys >= c.num_pages) return;
+    const float2 x = reinterpret_cast<const float2 *>(src + (int64_t)row * kDim)[lane];
+    uint8_t *pool = wave == 0 ? c.k_pages : c.v_pages;
+    if (c.kv_format == 0)
+      mx_store_row(x, pool + (int64_t)phys * kMxPageBytes, pos % kTokens, lane);
+    else
+      f8_store_row(x, pool + (int64_t)phys * kF8PageBytes, pos % kTokens, lane);
+  } else if (q8) {
+    const int64_t end = (int64_t)(row + 1) * H * kDim;   // this row's elements: [row H 128, end)
+    for (int64_t i = (int64_t)row * H * kDim + 4 * (tid - 128); i < end; i += 4 * 128) pack_q4(q, q_dtype, end, q8, i);
+  }
+}
+
+hipError_t launch_reuse_store(const CacheView &c, const float *k_new, const float *v_new, const void *q, int q_dtype,
+                              int32_t H, uint8_t *q8, uint32_t *counters, int32_t B, int32_t q_rows, hipStream_t s) {
+  if (B * q_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_reuse_store, dim3((unsigned)(B * q_rows)), dim3(256), 0, s, c, k_new, v_new, q, q_dtype, H, q8,
+                     counters, q_rows);
+  return hipGetLastError();
 }
 
 hipError_t launch_row_store(int format, const float *rows, int64_t n, const int64_t *slots,

@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_stages():
     names = declared_functions()
     for f in ["mxfp4_row_store", "fp8_row_store", "pack_q_e4m3", "index_score", "topk_blocks",
-              "index_score_topk", "sparse_split_attn", "lse_merge", "decode_step", "mxs_workspace_bytes",
+              "index_score_topk", "sparse_split_attn", "lse_merge", "decode_step", "decode_step_reuse",
+              "mxs_workspace_bytes",
               "mxs_default_partitions", "mxs_status_str", "mxs_last_error", "mxs_abi_version",
               "mxs_score_workspace_bytes"]:
         assert f in names, f
@@ -123,3 +124,26 @@ def test_decode_step_workspace_check(L):
     s.q_dtype = mx.MXS_F32
     s.B = 0                           # an empty batch does nothing and succeeds
     assert L.decode_step(ctypes.byref(s), None, 0, None) == mx.MXS_OK
+
+
+def test_decode_step_reuse_rejects_before_launch(L):
+    P = ctypes.byref
+    s = mx.StepStruct(_cache(idx_pages=0), 0, 0, 0, 4096, mx.MXS_F32, 0, 0, 2, 8, 16, 0, 32, 0, 0.1, 16384, 0, 0, 0)
+    need = L.mxs_workspace_bytes(2, 8, 16, 1, 32, 16, 0)
+    ws, table = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 16)
+    assert L.decode_step_reuse(P(s), None, ws, need, None) == mx.MXS_EINVAL
+    assert "block_table" in _err(L)
+    assert L.decode_step_reuse(P(s), table, ws, need - 1, None) == mx.MXS_EWORKSPACE
+    assert L.decode_step_reuse(P(s), ctypes.c_void_p((1 << 16) + 2), ws, need, None) == mx.MXS_EINVAL
+    s.k_new = 4096                    # K rows without V rows
+    assert L.decode_step_reuse(P(s), table, ws, need, None) == mx.MXS_EINVAL
+    assert "both or neither" in _err(L)
+    s.k_new = 0
+    s.topk = 65
+    assert L.decode_step_reuse(P(s), table, ws, need, None) == mx.MXS_EUNSUPPORTED
+    s.topk = 32
+    s.q_dtype = mx.MXS_E4M3
+    assert L.decode_step_reuse(P(s), table, ws, need, None) == mx.MXS_EUNSUPPORTED
+    s.q_dtype = mx.MXS_F32
+    s.B = 0                           # an empty batch does nothing and succeeds
+    assert L.decode_step_reuse(P(s), table, None, 0, None) == mx.MXS_OK

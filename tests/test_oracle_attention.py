@@ -154,3 +154,49 @@ def test_step_poison_vs_zero_tails_identical():
     r2 = S.decode_step_ref(inp, pools=zero)
     np.testing.assert_array_equal(r["O"], r2["O"])
     np.testing.assert_array_equal(r["block_table"], r2["block_table"])
+
+
+# ---------------------------------------------------------------- a step that reuses a selection
+def test_reuse_step_with_its_own_selection_is_the_full_step():
+    """A layer that reuses the block selection the full step would make gets the
+    full step's attention output and K / V pages, bit for bit."""
+    inp = _tiny(q=3)
+    r = S.decode_step_ref(inp)
+    r2 = S.decode_step_reuse_ref(inp, r["block_table"])
+    np.testing.assert_array_equal(r2["O"], r["O"])
+    np.testing.assert_array_equal(r2["lse"], r["lse"])
+    np.testing.assert_array_equal(r2["q8"], r["q8"])
+    for s in ("k", "v"):
+        np.testing.assert_array_equal(r2["pools"][s], r["pools"][s])
+    assert "idx" not in r2["pools"]
+
+
+def test_reuse_step_over_every_block_is_causal_dense_attention():
+    """Every block listed: each row is plain causal attention over the whole
+    dequantized cache (torch SDPA over positions <= the row's position)."""
+    inp = _tiny(q=3, topk=16)
+    L = int(inp.contexts[0])
+    table = np.tile(np.arange(16), (1, 3, 1))
+    r = S.decode_step_reuse_ref(inp, table)
+    K = F.mxfp4_read(r["pools"]["k"], inp.page_table[0], L)
+    V = F.mxfp4_read(r["pools"]["v"], inp.page_table[0], L)
+    qa, _ = S.attention_query(inp)
+    for j in range(3):
+        pos = L - 3 + j
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(qa[0, j])[None, :, None],
+            torch.from_numpy(K[:pos + 1])[None, None].expand(1, 4, pos + 1, 128),
+            torch.from_numpy(V[:pos + 1])[None, None].expand(1, 4, pos + 1, 128), scale=1 / np.sqrt(128))[0, :, 0]
+        np.testing.assert_allclose(r["O"][0, j], ref.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_reuse_step_skips_empty_and_out_of_range_entries():
+    inp = _tiny(q=2, topk=6)
+    clean = np.array([[[3, 7, 9, 15, -1, -1], [3, 7, 9, 15, -1, -1]]])
+    noisy = np.array([[[-1, 3, 400, 7, -7, 9], [15, 3, 7, 9, 16, 10**6]]])
+    noisy[0, 0, 2] = 400                                  # 400 * 128 is past every position
+    noisy[0, 0, 4] = 15
+    a = S.decode_step_reuse_ref(inp, clean)
+    b = S.decode_step_reuse_ref(inp, noisy)
+    np.testing.assert_allclose(b["O"], a["O"], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(b["lse"], a["lse"], rtol=1e-12)
