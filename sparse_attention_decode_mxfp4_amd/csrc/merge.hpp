@@ -38,11 +38,12 @@ constexpr int kCoherentBits = 16;                     // sc1
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float *base, int32_t n_floats) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, n_floats * 4, 0x00020000);
 }
+// (the builtins move raw 32-bit words: every value crosses as its bits)
 __device__ __forceinline__ f32x4 load4_coherent(__amdgpu_buffer_rsrc_t rs, int32_t float_off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(rs, float_off * 4, 0, kCoherentBits);
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, float_off * 4, 0, kCoherentBits));
 }
 __device__ __forceinline__ void store4_coherent(__amdgpu_buffer_rsrc_t rs, int32_t float_off, f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, rs, float_off * 4, 0, kCoherentBits);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, float_off * 4, 0, kCoherentBits);
 }
 
 template <bool COHERENT = false>

@@ -158,3 +158,30 @@ def test_reuse_step_empty_table(mx):
     table = np.full((wl.B, wl.q, wl.topk), -1)
     g = run_reuse(mx, inp, table)
     assert (g["O"] == 0).all() and np.isneginf(g["lse"]).all()
+
+
+def test_reuse_step_alternating_tables_share_a_workspace(mx):
+    """Two reuse steps over different tables alternate on one workspace: every
+    run equals its own first run bit for bit."""
+    import workloads.gpu as WG
+    inp = W.make_inputs(W.WORKLOADS["mxfp4_65k"])
+    wl = inp.wl
+    pools = WG.fill_prefix(inp, WG.empty_pools(inp))
+    cache = WG.make_cache(inp, pools)
+    t = WG.step_tensors(inp)
+    nb = mx.workspace_bytes(wl.B, wl.q, wl.H, 1, wl.topk, cache.stride)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    tabs = [torch.from_numpy(random_table(inp, s).astype(np.int32)).cuda() for s in (1, 2)]
+    steps = [mx.DecodeStepReuse(cache, t["query"], tb, wl.sm_scale, k_new=t.get("k_new"), v_new=t.get("v_new"),
+                                ws=ws) for tb in tabs]
+    first = []
+    for s_ in steps:
+        s_.run()
+        torch.cuda.synchronize()
+        first.append((s_.out.clone(), s_.lse.clone()))
+    for i in range(100):
+        for k, s_ in enumerate(steps):
+            s_.run()
+            assert torch.equal(s_.out, first[k][0]) and torch.equal(s_.lse, first[k][1]), f"run {i}, step {k}"
+    r = OS.decode_step_reuse_ref(inp, random_table(inp, 1), seqs=[0])
+    PT.check_attention(first[0][0].float().cpu().numpy()[0], r["O"][0], "alternating reuse b=0")

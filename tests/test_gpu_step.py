@@ -167,3 +167,36 @@ def test_decode_step_repeats_bit_exact(mx, name):
     O = out0.float().cpu().numpy()
     for b in range(wl.B):
         PT.check_attention(O[b], r["O"][b], f"{name} b={b}")
+
+
+@pytest.mark.parametrize("name", ["mxfp4_65k", "fp8"])
+def test_decode_step_alternating_inputs_share_a_workspace(mx, name):
+    """Two steps with different queries run alternately on one workspace: each
+    run's output and lse equal its own first run bit for bit, so no merge ever
+    reads a partial left in the workspace (or in a cache) by the other step's
+    previous run."""
+    import workloads.gpu as WG
+    inp = W.make_inputs(W.WORKLOADS[name].with_(B=4))
+    wl = inp.wl
+    pools = WG.fill_prefix(inp, WG.empty_pools(inp))
+    cache = WG.make_cache(inp, pools)
+    t = WG.step_tensors(inp)
+    qb = (t["query"].float() * -0.75 + 0.5).to(t["query"].dtype).contiguous()
+    nb = mx.workspace_bytes(wl.B, wl.q, wl.H, wl.H_I, wl.topk, cache.stride)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    kw = dict(k_new=t.get("k_new"), v_new=t.get("v_new"), idx_new=t.get("idx_new"), ws=ws)
+    steps = [mx.DecodeStep(cache, q, t["q_idx"], t["w"], wl.topk, wl.sm_scale, **kw) for q in (t["query"], qb)]
+    first = []
+    for s_ in steps:
+        s_.run()
+        torch.cuda.synchronize()
+        first.append((s_.out.clone(), s_.lse.clone()))
+    assert not torch.equal(first[0][0], first[1][0])
+    for i in range(100):
+        for k, s_ in enumerate(steps):
+            s_.run()
+            assert torch.equal(s_.out, first[k][0]) and torch.equal(s_.lse, first[k][1]), f"run {i}, step {k}"
+    r = OS.decode_step_ref(inp, seqs=[0, 1])
+    O = first[0][0].float().cpu().numpy()
+    for b in (0, 1):
+        PT.check_attention(O[b], r["O"][b], f"{name} b={b}")
