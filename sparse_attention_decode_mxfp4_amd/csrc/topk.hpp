@@ -16,14 +16,15 @@
 //      sorts its 64 maxima, and each wave merges the four sorted lists itself
 //      (bitonic half-cleaners), so no wave waits for another beyond one barrier;
 //   2. every candidate with key >= T0 (typically a few dozen) is compacted
-//      into LDS (per-wave ballot offsets, one barrier for the wave totals);
-//   3. exactly k survivors are the selection; when at most 64 survive, every
-//      wave sorts them by (key descending, id ascending) across its lanes and
-//      keeps the first k; with more survivors (ties at the bound) each
-//      survivor is ranked against all of them through LDS first; the selected
-//      ids are sorted ascending across the lanes.
-// All cross-lane exchanges are DPP row permutes and gfx950 permlane swaps
-// (no LDS round trip per step).
+//      into LDS in ascending id order (id = tid + 256 r ascends with (r, wave,
+//      lane): per-(r, wave) ballot counts, one barrier for the counts);
+//   3. exactly k survivors are the selection, already ascending; when at most
+//      64 survive, every wave holds them one per lane, finds the k-th largest
+//      key T1 (a sort of the keys across the lanes), keeps the keys above T1
+//      and, of those equal to T1, the lowest ids (lane order), and packs the
+//      kept ids to the front (one forward lane permute), which leaves them
+//      ascending; with more survivors (ties at the bound) each survivor is
+//      ranked against all of them through LDS and the ids are sorted after.
 #pragma once
 
 #include "common.hpp"
@@ -74,27 +75,6 @@ __device__ __forceinline__ uint32_t merge64(uint32_t v) {
   return bitonic_stage<DESC, 64, 32>(v, threadIdx.x & 63);
 }
 
-template <int SIZE, int ST>
-__device__ __forceinline__ uint64_t bitonic_stage_desc_u64(uint64_t v, int lane) {
-  if constexpr (ST == 0) {
-    return v;
-  } else {
-    const uint64_t o = ((uint64_t)xor_lane<ST>((uint32_t)(v >> 32)) << 32) | xor_lane<ST>((uint32_t)v);
-    const bool lower = (lane & ST) == 0;
-    const bool first = (lane & SIZE) == 0;
-    return bitonic_stage_desc_u64<SIZE, ST / 2>((lower == first) ? (v > o ? v : o) : (v < o ? v : o), lane);
-  }
-}
-
-template <int SIZE = 2>
-__device__ __forceinline__ uint64_t sort64_desc_u64(uint64_t v) {
-  if constexpr (SIZE > 64) {
-    return v;
-  } else {
-    return sort64_desc_u64<SIZE * 2>(bitonic_stage_desc_u64<SIZE, SIZE / 2>(v, threadIdx.x & 63));
-  }
-}
-
 // Workgroup barrier for LDS data only: the LDS writes are waited for, vector
 // memory operations are not (unlike __syncthreads, which would also wait for
 // every global load still in flight).
@@ -102,10 +82,10 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 template <int ITEMS>
 struct TopkSmem {
-  uint32_t key[kTopkThreads * ITEMS];      // survivors (any order)
+  uint32_t key[kTopkThreads * ITEMS];      // survivors, ascending id
   uint16_t idx[kTopkThreads * ITEMS];
   uint32_t wmax[4][64];                    // each wave's thread maxima, sorted descending
-  uint32_t wtot[4];                        // survivors per wave
+  alignas(16) uint32_t wcnt[ITEMS][4];     // survivors of item r in wave w (read 16 B at a time)
   uint32_t by_rank[64];                    // many-survivor path: id of rank r
 };
 
@@ -138,28 +118,24 @@ __device__ __forceinline__ uint32_t wg_topk(const float (&v)[ITEMS], int n_cand,
   const uint32_t e = merge64<true>(max(c, d));                                        // of all four
   const uint32_t T0 = (uint32_t)__builtin_amdgcn_readlane((int)e, topk - 1);
 
-  // 2. compact the survivors: per-wave ballot offsets, then the wave bases
+  // 2. compact the survivors in ascending id order: item r of wave w lands
+  //    after every survivor of items < r and of item r in waves < w
   bool keep[ITEMS];
   uint32_t at[ITEMS];
-  uint32_t wave_n = 0;
 #pragma unroll
   for (int r = 0; r < ITEMS; ++r) {
     keep[r] = tid + kTopkThreads * r < n_cand && key[r] >= T0;
     const uint64_t bal = __ballot(keep[r]);
-    at[r] = wave_n + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-    wave_n += (uint32_t)__popcll(bal);
+    at[r] = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    if (lane == 0) sm.wcnt[r][wave] = (uint32_t)__popcll(bal);
   }
-  if (lane == 0) sm.wtot[wave] = wave_n;
   lds_barrier();
-  uint32_t base = 0, n_surv = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t n = sm.wtot[w];
-    base += w < wave ? n : 0u;
-    n_surv += n;
-  }
+  uint32_t n_surv = 0;
 #pragma unroll
   for (int r = 0; r < ITEMS; ++r) {
+    const u32x4 c = *reinterpret_cast<const u32x4 *>(sm.wcnt[r]);
+    const uint32_t base = n_surv + (wave > 0 ? c[0] : 0u) + (wave > 1 ? c[1] : 0u) + (wave > 2 ? c[2] : 0u);
+    n_surv += c[0] + c[1] + c[2] + c[3];
     if (keep[r]) {
       sm.key[base + at[r]] = key[r];
       sm.idx[base + at[r]] = (uint16_t)(tid + kTopkThreads * r);
@@ -167,29 +143,36 @@ __device__ __forceinline__ uint32_t wg_topk(const float (&v)[ITEMS], int n_cand,
   }
   lds_barrier();
 
-  // 3. exact selection by (key descending, id ascending)
-  uint32_t sel;
-  if (n_surv == (uint32_t)topk) {            // exactly k survive: all selected
-    sel = (uint32_t)lane < n_surv ? (uint32_t)sm.idx[lane] : 0xFFFFFFFFu;
-  } else if (n_surv <= 64u) {
+  // 3. exact selection by (key descending, id ascending), ids kept ascending
+  if (n_surv == (uint32_t)topk)              // exactly k survive: all selected
+    return (uint32_t)lane < n_surv ? (uint32_t)sm.idx[lane] : 0xFFFFFFFFu;
+  if (n_surv <= 64u) {
     const bool have = (uint32_t)lane < n_surv;
-    const uint32_t ks = have ? sm.key[lane] : 0u, is = have ? (uint32_t)sm.idx[lane] : 0u;
-    const uint64_t comp = sort64_desc_u64(have ? (((uint64_t)ks << 32) | (0xFFFFFFFFu - is)) : 0ull);
-    sel = lane < topk ? 0xFFFFFFFFu - (uint32_t)comp : 0xFFFFFFFFu;
-  } else {                                   // ties at the bound: rank through LDS
-    for (uint32_t i = tid; i < n_surv; i += kTopkThreads) {
-      const uint32_t ki = sm.key[i], ii = sm.idx[i];
-      uint32_t rank = 0;
-      for (uint32_t o = 0; o < n_surv; ++o) {
-        const uint32_t ko = sm.key[o];
-        rank += (ko > ki) || (ko == ki && sm.idx[o] < ii);
-      }
-      if (rank < (uint32_t)topk) sm.by_rank[rank] = ii;
-    }
-    lds_barrier();
-    sel = lane < topk ? sm.by_rank[lane] : 0xFFFFFFFFu;
+    const uint32_t ks = have ? sm.key[lane] : 0u, is = have ? (uint32_t)sm.idx[lane] : 0xFFFFFFFFu;
+    const uint32_t T1 = (uint32_t)__builtin_amdgcn_readlane((int)sort64<true>(ks), topk - 1);
+    const uint64_t gt = __ballot(have && ks > T1), eq = __ballot(have && ks == T1);
+    const uint32_t eq_below =
+        __builtin_amdgcn_mbcnt_hi((uint32_t)(eq >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eq, 0u));
+    const bool take = have && (ks > T1 || (ks == T1 && eq_below < (uint32_t)topk - (uint32_t)__popcll(gt)));
+    // stable partition: taken lanes to the front (ascending ids), the rest after
+    const uint64_t tb = __ballot(take);
+    const uint32_t before = __builtin_amdgcn_mbcnt_hi((uint32_t)(tb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)tb, 0u));
+    const uint32_t dst = take ? before : (uint32_t)__popcll(tb) + (uint32_t)lane - before;
+    const uint32_t got = (uint32_t)__builtin_amdgcn_ds_permute((int)(dst * 4u), (int)is);
+    return lane < topk ? got : 0xFFFFFFFFu;
   }
-  return sort64<false>(sel);                 // ascending ids
+  // ties at the bound: rank through LDS, then sort the selected ids
+  for (uint32_t i = tid; i < n_surv; i += kTopkThreads) {
+    const uint32_t ki = sm.key[i], ii = sm.idx[i];
+    uint32_t rank = 0;
+    for (uint32_t o = 0; o < n_surv; ++o) {
+      const uint32_t ko = sm.key[o];
+      rank += (ko > ki) || (ko == ki && sm.idx[o] < ii);
+    }
+    if (rank < (uint32_t)topk) sm.by_rank[rank] = ii;
+  }
+  lds_barrier();
+  return sort64<false>(lane < topk ? sm.by_rank[lane] : 0xFFFFFFFFu);   // ascending ids
 }
 
 }  // namespace mxs

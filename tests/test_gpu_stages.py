@@ -176,16 +176,18 @@ def test_index_score_one_hot_structure(mx):
                     OI.n_candidates(700, 3))
 
 
+@pytest.mark.parametrize("stride", [300, 2000, 2100])
 @pytest.mark.parametrize("k", [1, 4, 16, 32, 64])
-def test_topk_exact_on_given_scores(mx, k):
+def test_topk_exact_on_given_scores(mx, k, stride):
     """Top-k of the same fp32 scores: the GPU selection equals the oracle's
-    exactly, including heavy ties (ties go to the lower block id) and rows
-    with fewer candidates than k."""
-    rng = np.random.default_rng(k)
-    B, q, stride = 5, 8, 2100
+    exactly, including heavy ties (ties go to the lower block id), a few ties
+    at the k-th score, and rows with fewer candidates than k."""
+    rng = np.random.default_rng(k + stride)
+    B, q = 5, 8
     ctx = np.array([stride * 128, 1000, 128 * 64 + 3, 77, 128 * 2000], dtype=np.int64)
     S = rng.integers(-20, 20, size=(B, q, stride)).astype(np.float32)          # many ties
     S[1] = rng.standard_normal((q, stride)).astype(np.float32)
+    S[3] = (np.round(rng.standard_normal((q, stride)) * 6) / 6).astype(np.float32)   # some ties near the top
     S[4, :, :] = 1.0                                                            # all equal
     S[0, 3, ::7] = -np.inf
     table = np.zeros((B, stride), dtype=np.int32)
