@@ -56,13 +56,6 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
   const bf16x2 v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
 }
-// Four e4m3 codes (one dword) as two dwords of bf16 pairs, element order
-// kept (v_cvt_scalef32_pk_bf16_fp8 with scale 1: exact, e4m3 has 3 mantissa
-// bits; 0x7F / 0xFF give NaN).
-__device__ __forceinline__ uint2 e4m3x4_bf16(uint32_t d) {
-  return make_uint2(bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, false)),
-                    bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, true)));
-}
 // fp32 value of an e8m0 scale byte for the cvt_scalef32 instructions:
 // byte << 23 is 2^(byte - 127) for byte >= 1, and byte 0 takes 0x400000 = 2^-127.
 __device__ __forceinline__ float e8m0_scale(uint32_t byte) { return u2f(max(byte << 23, 0x00400000u)); }
@@ -142,7 +135,7 @@ __device__ __forceinline__ void query_operands(const QueryRegs<FMT> &q, int H, i
   for (int s = 0; s < 4; ++s) {
     u32x4 v;
     if constexpr (FMT == 0) {
-      const uint2 x = e4m3x4_bf16(q.c[s].x), y = e4m3x4_bf16(q.c[s].y);
+      const uint2 x = e4m3x4_to_bf16(q.c[s].x), y = e4m3x4_to_bf16(q.c[s].y);
       v = u32x4{x.x, x.y, y.x, y.y};
     } else {
       v = q.c[s];
@@ -189,8 +182,8 @@ __device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t
         a = u32x4{w4[0], w4[1], w4[2], w4[3]};
       } else {
         const u32x4 &src = r.k[nt][s >> 1];
-        const uint2 x = e4m3x4_bf16(live ? src[2 * (s & 1)] : 0u);
-        const uint2 y = e4m3x4_bf16(live ? src[2 * (s & 1) + 1] : 0u);
+        const uint2 x = e4m3x4_to_bf16(live ? src[2 * (s & 1)] : 0u);
+        const uint2 y = e4m3x4_to_bf16(live ? src[2 * (s & 1) + 1] : 0u);
         a = u32x4{x.x, x.y, y.x, y.y};
       }
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qbf[s], acc, 0, 0, 0);
@@ -258,7 +251,7 @@ __device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t
         const uint32_t sb = __builtin_amdgcn_ubfe(r.vs[s][e >> 2][e & 3], 8 * (n >> 2), 8);
         fp4x8_to_bf16(live ? r.v[s][e] : 0u, e8m0_scale(live ? sb : 127u), W[e]);
       } else {
-        const uint2 x = e4m3x4_bf16(live ? r.v[s][e].x : 0u), y = e4m3x4_bf16(live ? r.v[s][e].y : 0u);
+        const uint2 x = e4m3x4_to_bf16(live ? r.v[s][e].x : 0u), y = e4m3x4_to_bf16(live ? r.v[s][e].y : 0u);
         W[e][0] = x.x;
         W[e][1] = x.y;
         W[e][2] = y.x;

@@ -93,21 +93,12 @@ __device__ __forceinline__ void fp4x8_to_bf16(uint32_t packed, float scale_f32, 
   out[3] = bf16x2_bits(MXS_CVT_FP4_BF16(packed, scale_f32, 3));
 }
 
-// e4m3 code -> bf16 bits (exact: e4m3 has 3 mantissa bits). Branch-free, so
-// that loads around it are not split by divergent control flow.
-__device__ __forceinline__ uint32_t e4m3_bf16_bits(uint32_t c) {
-  const uint32_t s = (c & 0x80u) << 8;
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  const uint32_t normal = s | ((e + 120u) << 7) | (m << 4);
-  const uint32_t sub = s | (f2u((float)m * 0.001953125f) >> 16);     // m * 2^-9
-  const uint32_t r = e == 0u ? sub : normal;
-  return (c & 0x7Fu) == 0x7Fu ? (s | 0x7FC0u) : r;                   // 0x7F / 0xFF: NaN
-}
-
-// Four e4m3 codes (one dword) -> two dwords of bf16 pairs, element order kept.
+// Four e4m3 codes (one dword) -> two dwords of bf16 pairs, element order kept
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1: exact, e4m3 has 3 mantissa bits;
+// 0x7F / 0xFF give NaN; checked against a bit-level decode on all 256 codes).
 __device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t d) {
-  return make_uint2(e4m3_bf16_bits(d & 0xFFu) | (e4m3_bf16_bits((d >> 8) & 0xFFu) << 16),
-                    e4m3_bf16_bits((d >> 16) & 0xFFu) | (e4m3_bf16_bits(d >> 24) << 16));
+  return make_uint2(bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, false)),
+                    bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, true)));
 }
 
 // ---------------------------------------------------------------- wave helpers
