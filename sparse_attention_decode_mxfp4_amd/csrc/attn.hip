@@ -505,7 +505,7 @@ __global__ __launch_bounds__(256) void k_select_attn(CacheView c, const float *_
              (uint32_t)(P - 1);
   lds_barrier();
   if (!s_last) return;
-  merge_row<true>(sp_m, sp_l, sp_o, row, H, P, fm.out, fm.lse);
+  merge_row(sp_m, sp_l, sp_o, row, H, P, fm.out, fm.lse);
 }
 
 hipError_t launch_split_attn(const CacheView &c, const void *q, int q_dtype, const int32_t *block_table,

@@ -131,14 +131,4 @@ __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
 }
 
 
-__device__ __forceinline__ float wave_max16(float v) {      // max over the 16 lanes sharing lane / 16
-  v = fmaxf(v, __shfl_xor(v, 1));
-  v = fmaxf(v, __shfl_xor(v, 2));
-  v = fmaxf(v, __shfl_xor(v, 4));
-  v = fmaxf(v, __shfl_xor(v, 8));
-  return v;
-}
-
-__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63u; }
-
 }  // namespace mxs

@@ -1,34 +1,16 @@
-// Log-sum-exp merge of split partials for one (query row, head), one wave
-// (ATOM PR #2812, "Mono decode over the MXFP4 KV and index caches", commit
-// message of the MXFP4 main-KV commit: the merge consumes sp_o / sp_m / sp_l).
+// Log-sum-exp merge of split partials (ATOM PR #2812, "Mono decode over the
+// MXFP4 KV and index caches", commit message of the MXFP4 main-KV commit: the
+// merge consumes sp_o / sp_m / sp_l):
 //   M = max_p m_p;  L = sum_p l_p e^(m_p - M);  O = sum_p o_p e^(m_p - M) / L;
 //   lse = M + ln L.  Empty partitions (m_p = -inf) weigh nothing.
-// Lane p < P reads partition p's (m, l); each lane owns two output elements.
+// merge_one: one (query row, head) per wave (the stand-alone merge kernel);
+// lane p < P reads partition p's (m, l), each lane owns two output elements.
+// merge_row: one query row per workgroup (the decode step's in-launch merge).
 #pragma once
 
 #include "common.hpp"
 
 namespace mxs {
-
-// COHERENT: the partials are read with agent-scope loads (written by other
-// workgroups of the same launch with agent-scope stores).
-template <bool COHERENT>
-__device__ __forceinline__ float get(const float *p) {
-  if constexpr (COHERENT)
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else
-    return *p;
-}
-template <bool COHERENT>
-__device__ __forceinline__ float2 get2(const float2 *p) {
-  if constexpr (COHERENT) {
-    const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    return make_float2(u2f((uint32_t)u), u2f((uint32_t)(u >> 32)));
-  } else {
-    return *p;
-  }
-}
 
 // Device-coherent 16-byte partial traffic for the decode step's in-launch
 // merge: buffer loads / stores with the sc1 cache-policy bit (the bit an
@@ -42,21 +24,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float *base, in
 __device__ __forceinline__ f32x4 load4_coherent(__amdgpu_buffer_rsrc_t rs, int32_t float_off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, float_off * 4, 0, kCoherentBits));
 }
+__device__ __forceinline__ float load1_coherent(__amdgpu_buffer_rsrc_t rs, int32_t float_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, float_off * 4, 0, kCoherentBits));
+}
 __device__ __forceinline__ void store4_coherent(__amdgpu_buffer_rsrc_t rs, int32_t float_off, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, float_off * 4, 0, kCoherentBits);
 }
 
-template <bool COHERENT = false>
 __device__ __forceinline__ void merge_one(const float *__restrict__ sp_m, const float *__restrict__ sp_l,
                                           const float *__restrict__ sp_o, int64_t r, int32_t P, int lane,
                                           uint16_t *__restrict__ out, float *__restrict__ lse) {
   const float NEG_INF = -__builtin_inff();
-  const float mraw = get<COHERENT>(sp_m + r * P + min(lane, P - 1));
-  const float lraw = get<COHERENT>(sp_l + r * P + min(lane, P - 1));
+  const float mraw = sp_m[r * P + min(lane, P - 1)];
+  const float lraw = sp_l[r * P + min(lane, P - 1)];
   const float2 *po = reinterpret_cast<const float2 *>(sp_o + r * P * kDim) + lane;
   float2 v[8];                                  // the first 8 partitions' outputs, requested with (m, l)
 #pragma unroll
-  for (int u = 0; u < 8; ++u) v[u] = get2<COHERENT>(po + min(u, P - 1) * (kDim / 2));   // clamped: no branch
+  for (int u = 0; u < 8; ++u) v[u] = po[min(u, P - 1) * (kDim / 2)];   // clamped: no branch
   const float mp = lane < P ? mraw : NEG_INF;
   float M = mp;
 #pragma unroll
@@ -70,7 +54,7 @@ __device__ __forceinline__ void merge_one(const float *__restrict__ sp_m, const 
   for (int p0 = 0; p0 < P; p0 += 8) {
     if (p0 > 0) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = get2<COHERENT>(po + min(p0 + u, P - 1) * (kDim / 2));
+      for (int u = 0; u < 8; ++u) v[u] = po[min(p0 + u, P - 1) * (kDim / 2)];
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -81,25 +65,18 @@ __device__ __forceinline__ void merge_one(const float *__restrict__ sp_m, const 
       }
     }
   }
-  a0 *= inv;
-  a1 *= inv;
-  const uint32_t u0 = f2u(a0), u1 = f2u(a1);
-  const uint32_t b0 = (u0 + 0x7FFFu + ((u0 >> 16) & 1u)) >> 16;   // round to nearest even
-  const uint32_t b1 = (u1 + 0x7FFFu + ((u1 >> 16) & 1u)) >> 16;
-  reinterpret_cast<uint32_t *>(out + r * kDim)[lane] = b0 | (b1 << 16);
+  const bf16x2 o = {(__bf16)(a0 * inv), (__bf16)(a1 * inv)};     // round to nearest even (v_cvt_pk_bf16_f32)
+  reinterpret_cast<uint32_t *>(out + r * kDim)[lane] = bf16x2_bits(o);
   if (lse && lane == 0) lse[r] = Lp > 0.0f ? M + __logf(Lp) : NEG_INF;
 }
-
-}  // namespace mxs
-
-namespace mxs {
 
 // One query row (H <= 16 heads) merged by a 256-thread workgroup: thread t
 // takes head t / 16 and output elements 8 (t % 16) .. + 7. Every partition's
 // (m, l) and the thread's 8 elements of every partition's O are requested at
 // once, 8 partitions per round (more partitions fold in with an online
-// rescale), so the merge costs one memory round trip for P <= 8.
-template <bool COHERENT>
+// rescale), so the merge costs one memory round trip for P <= 8. The
+// partials were written by other workgroups of the same launch (device-
+// coherent stores), so every load is device-coherent too.
 __device__ __forceinline__ void merge_row(const float *__restrict__ sp_m, const float *__restrict__ sp_l,
                                           const float *__restrict__ sp_o, int64_t row, int32_t H, int32_t P,
                                           uint16_t *__restrict__ out, float *__restrict__ lse) {
@@ -119,7 +96,7 @@ __device__ __forceinline__ void merge_row(const float *__restrict__ sp_m, const 
   for (int p0 = 0; p0 < P; p0 += 8) {
     float m[8], l[8];
     f32x4 o[8][2];
-    if (COHERENT && ml4) {
+    if (ml4) {
       const f32x4 m0 = load4_coherent(rm, h * P + p0), m1 = load4_coherent(rm, h * P + p0 + 4);
       const f32x4 l0 = load4_coherent(rl, h * P + p0), l1 = load4_coherent(rl, h * P + p0 + 4);
 #pragma unroll
@@ -133,8 +110,8 @@ __device__ __forceinline__ void merge_row(const float *__restrict__ sp_m, const 
 #pragma unroll
       for (int u = 0; u < 8; ++u) {               // clamped, unconditional
         const int pp = min(p0 + u, P - 1);
-        m[u] = get<COHERENT>(sp_m + r * P + pp);
-        l[u] = get<COHERENT>(sp_l + r * P + pp);
+        m[u] = load1_coherent(rm, h * P + pp);
+        l[u] = load1_coherent(rl, h * P + pp);
       }
     }
 #pragma unroll
@@ -142,12 +119,7 @@ __device__ __forceinline__ void merge_row(const float *__restrict__ sp_m, const 
       const int pp = min(p0 + u, P - 1);
       const int32_t off = (h * P + pp) * kDim + e0;
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        if constexpr (COHERENT)
-          o[u][k] = load4_coherent(ro, off + 4 * k);
-        else
-          o[u][k] = *reinterpret_cast<const f32x4 *>(sp_o + row * H * P * kDim + off + 4 * k);
-      }
+      for (int k = 0; k < 2; ++k) o[u][k] = load4_coherent(ro, off + 4 * k);
     }
     float Mc = M;
 #pragma unroll
