@@ -11,7 +11,11 @@
 // * Workgroup = (partition p, query row j, sequence b), 4 waves. Partition p
 //   owns block-table slots [p c, min((p+1) c, topk)), c = ceil(topk / P); wave
 //   w takes every 4th of them, keeps an online softmax (m, l, O) for the 16
-//   heads, and the 4 waves merge through LDS into one partial.
+//   heads, and the 4 waves merge through LDS into one partial. (The block
+//   code also takes a wave's share as half a block, for a workgroup of 8
+//   waves in pairs; measured on MI355X that made the step's launch slower:
+//   the 8-wave selection and merge lose more at their barriers than the
+//   halved block work gains.)
 // * QK: D[token][head] = K[token][:] . q[head][:] on v_mfma_f32_16x16x32_bf16.
 //   Lane 16 kg + n loads token n's group kg — 16 bytes and one scale byte, the
 //   same coalesced pattern as the index scorer — and widens it to bf16 with
@@ -39,10 +43,13 @@
 #include "launch.hpp"
 #include "topk.hpp"
 #include "merge.hpp"
+#include "mxsparse.h"
 
 namespace mxs {
 
-constexpr int kAttnWaves = 4;
+constexpr int kAttnWaves = 4;    // the stand-alone split stage
+constexpr int kStepWaves = 4;    // the decode step's attention launch
+constexpr int kStepTiles = 8;    // 16-token tiles per wave and block (8: whole blocks)
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -60,49 +67,55 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
 // byte << 23 is 2^(byte - 127) for byte >= 1, and byte 0 takes 0x400000 = 2^-127.
 __device__ __forceinline__ float e8m0_scale(uint32_t byte) { return u2f(max(byte << 23, 0x00400000u)); }
 
-// One block's operands as this lane loads them (all requested before any math).
-//  K: tile nt -> token 16 nt + n; MXFP4: 16 bytes of group kg + its scale byte;
-//     FP8: 32 bytes (elements 32 kg .. + 31) + 4 token scales (tokens 16 nt + 4 kg + i).
-//  V: k-step s -> the 8 tokens te(s, e); MXFP4: 4 bytes (codes 8 n .. 8 n + 7) per
-//     token + the scale dwords of the two 4-token runs; FP8: 8 bytes per token +
-//     the fp32 scales of the two runs.
-template <int FMT> struct BlockRegs;
-template <> struct BlockRegs<0> { u32x4 k[8]; uint32_t ks[8]; uint32_t v[4][8]; u32x4 vs[4][2]; };
-template <> struct BlockRegs<1> { u32x4 k[8][2]; f32x4 ks[8]; uint2 v[4][8]; f32x4 vs[4][2]; };
+// The operands of a wave's token range of one block (NT 16-token tiles from
+// token toff of the page: the whole page, NT = 8, or one half, NT = 4), as this
+// lane loads them (all requested before any math).
+//  K: tile nt -> token toff + 16 nt + n; MXFP4: 16 bytes of group kg + its scale
+//     byte; FP8: 32 bytes (elements 32 kg .. + 31) + 4 token scales (tokens
+//     toff + 16 nt + 4 kg + i).
+//  V: k-step s -> the 8 tokens toff + te(s, e); MXFP4: 4 bytes (codes 8 n ..
+//     8 n + 7) per token + the scale dwords of the two 4-token runs; FP8: 8
+//     bytes per token + the fp32 scales of the two runs.
+template <int FMT, int NT> struct BlockRegs;
+template <int NT> struct BlockRegs<0, NT> { u32x4 k[NT]; uint32_t ks[NT]; uint32_t v[NT / 2][8]; u32x4 vs[NT / 2][2]; };
+template <int NT> struct BlockRegs<1, NT> { u32x4 k[NT][2]; f32x4 ks[NT]; uint2 v[NT / 2][8]; f32x4 vs[NT / 2][2]; };
 
 // token of element e of the lane's k-group in PV k-step s
 __device__ __forceinline__ int pv_token(int s, int kg, int e) { return 32 * s + (e < 4 ? 4 * kg + e : 16 + 4 * kg + e - 4); }
 
-template <int FMT>
-__device__ __forceinline__ void load_block(BlockRegs<FMT> &r, const uint8_t *kp, const uint8_t *vp, int n, int kg) {
+template <int FMT, int NT>
+__device__ __forceinline__ void load_block(BlockRegs<FMT, NT> &r, const uint8_t *kp, const uint8_t *vp, int toff, int n,
+                                           int kg) {
   if constexpr (FMT == 0) {
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const int tok = 16 * nt + n;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int tok = toff + 16 * nt + n;
       r.k[nt] = *reinterpret_cast<const u32x4 *>(kp + 64 * tok + 16 * kg);
       r.ks[nt] = kp[kMxScaleOff + 4 * tok + kg];
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < NT / 2; ++s) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) r.v[s][e] = *reinterpret_cast<const uint32_t *>(vp + 64 * pv_token(s, kg, e) + 4 * n);
-      r.vs[s][0] = *reinterpret_cast<const u32x4 *>(vp + kMxScaleOff + 4 * pv_token(s, kg, 0));
-      r.vs[s][1] = *reinterpret_cast<const u32x4 *>(vp + kMxScaleOff + 4 * pv_token(s, kg, 4));
+      for (int e = 0; e < 8; ++e)
+        r.v[s][e] = *reinterpret_cast<const uint32_t *>(vp + 64 * (toff + pv_token(s, kg, e)) + 4 * n);
+      r.vs[s][0] = *reinterpret_cast<const u32x4 *>(vp + kMxScaleOff + 4 * (toff + pv_token(s, kg, 0)));
+      r.vs[s][1] = *reinterpret_cast<const u32x4 *>(vp + kMxScaleOff + 4 * (toff + pv_token(s, kg, 4)));
     }
   } else {
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const int tok = 16 * nt + n;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int tok = toff + 16 * nt + n;
       r.k[nt][0] = *reinterpret_cast<const u32x4 *>(kp + 128 * tok + 32 * kg);
       r.k[nt][1] = *reinterpret_cast<const u32x4 *>(kp + 128 * tok + 32 * kg + 16);
-      r.ks[nt] = *reinterpret_cast<const f32x4 *>(kp + kF8ScaleOff + 4 * (16 * nt + 4 * kg));
+      r.ks[nt] = *reinterpret_cast<const f32x4 *>(kp + kF8ScaleOff + 4 * (toff + 16 * nt + 4 * kg));
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < NT / 2; ++s) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) r.v[s][e] = *reinterpret_cast<const uint2 *>(vp + 128 * pv_token(s, kg, e) + 8 * n);
-      r.vs[s][0] = *reinterpret_cast<const f32x4 *>(vp + kF8ScaleOff + 4 * pv_token(s, kg, 0));
-      r.vs[s][1] = *reinterpret_cast<const f32x4 *>(vp + kF8ScaleOff + 4 * pv_token(s, kg, 4));
+      for (int e = 0; e < 8; ++e)
+        r.v[s][e] = *reinterpret_cast<const uint2 *>(vp + 128 * (toff + pv_token(s, kg, e)) + 8 * n);
+      r.vs[s][0] = *reinterpret_cast<const f32x4 *>(vp + kF8ScaleOff + 4 * (toff + pv_token(s, kg, 0)));
+      r.vs[s][1] = *reinterpret_cast<const f32x4 *>(vp + kF8ScaleOff + 4 * (toff + pv_token(s, kg, 4)));
     }
   }
 }
@@ -145,19 +158,20 @@ __device__ __forceinline__ void query_operands(const QueryRegs<FMT> &q, int H, i
   }
 }
 
-// One selected block (page `phys`, first token position t0) folded into this
-// wave's online softmax state for head n = lane % 16: m_run (log2 units: the
-// logits times log2 e), l_run, O. FULL: every token of the block is at or
-// before the row's position (no masking). FIRST: the wave's first block
-// (nothing to rescale). `phys` is wave-uniform.
-template <int FMT, bool FULL, bool FIRST>
-__device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t0, int pos, const QueryRegs<FMT> &q,
-                                             int H, float qk_scale2, float &m_run, float &l_run, f32x4 O[8], int n,
-                                             int kg) {
+// The wave's token range of one selected block (page `phys`, 16 NT tokens
+// from page token toff, at positions t0 ..) folded into this wave's online
+// softmax state for head n = lane % 16: m_run (log2 units: the logits times
+// log2 e), l_run, O. FULL: every token of the range is at or before the row's
+// position (no masking); otherwise at least its first one is. FIRST: the
+// wave's first range (nothing to rescale). `phys` is wave-uniform.
+template <int FMT, bool FULL, bool FIRST, int NT>
+__device__ __forceinline__ void attend_block(const CacheView &c, int phys, int toff, int t0, int pos,
+                                             const QueryRegs<FMT> &q, int H, float qk_scale2, float &m_run,
+                                             float &l_run, f32x4 O[8], int n, int kg) {
   const float NEG_INF = -__builtin_inff();
   const int64_t pb = (int64_t)phys * (FMT == 0 ? kMxPageBytes : kF8PageBytes);
-  BlockRegs<FMT> r;
-  load_block<FMT>(r, c.k_pages + pb, c.v_pages + pb, n, kg);
+  BlockRegs<FMT, NT> r;
+  load_block<FMT, NT>(r, c.k_pages + pb, c.v_pages + pb, toff, n, kg);
   // The query is widened here, after the pages are requested: the empty asm
   // keeps the (loop-invariant) widening from being hoisted above these loads,
   // which would wait for the query before any page is requested.
@@ -168,9 +182,9 @@ __device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t
   query_operands<FMT>(qc, H, n, qbf);
 
   // ---- QK: scores (log2 units) of tokens 16 nt + 4 kg + i for head n
-  float sc[8][4];
+  float sc[NT][4];
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
     const bool live = FULL || t0 + 16 * nt + n <= pos;       // the lane's A row (token 16 nt + n)
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -199,7 +213,7 @@ __device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t
   // ---- online softmax for head n (base 2)
   float bm = NEG_INF;
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt)
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) bm = fmaxf(bm, sc[nt][i]);
   bm = fmaxf(bm, u2f(xor_lane<16>(f2u(bm))));
@@ -207,7 +221,7 @@ __device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t
   const float m_new = FIRST ? bm : fmaxf(m_run, bm);
   float ps = 0.f;
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt)
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       sc[nt][i] = __builtin_amdgcn_exp2f(sc[nt][i] - m_new);      // masked tokens: 2^-inf = 0
@@ -228,9 +242,9 @@ __device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t
   }
   m_run = m_new;
 
-  // ---- PV over 4 k-steps of 32 tokens
+  // ---- PV over NT / 2 k-steps of 32 tokens
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < NT / 2; ++s) {
     u32x4 pa;                                     // P of the lane's 8 tokens as bf16
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
@@ -272,39 +286,47 @@ __device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t
   }
 }
 
-// The wave's blocks: slots slot0 + wave, + 4, ... below slot1 of a block list
-// (blk_of(slot) -> block id or -1, phys_of(blk) -> page or -1), folded into
-// the wave's softmax state. The first valid block is peeled off the loop (a
-// loop header would make the first block's page requests wait for every
-// load still in flight, the query's included), and partly masked blocks take
-// their own code path.
-template <int FMT, class BlkOf, class PhysOf>
+// The wave's blocks of a block list (blk_of(slot) -> block id or -1,
+// phys_of(blk) -> page or -1) below slot1, folded into the wave's softmax
+// state. NW waves; each block is split into 8 / NT token ranges of 16 NT
+// tokens, one per wave of a group of 8 / NT consecutive waves, and wave group
+// g takes slots slot0 + g, slot0 + g + NW NT / 8, ... A range that starts past
+// the row's position is skipped (every range taken has a visible token). The
+// first range is peeled off the loop (a loop header would make its page
+// requests wait for every load still in flight, the query's included), and
+// partly masked ranges take their own code path.
+template <int FMT, int NW, int NT, class BlkOf, class PhysOf>
 __device__ __forceinline__ void attend_slots(const CacheView &c, int slot0, int slot1, int pos, const QueryRegs<FMT> &q,
                                              int H, float qk_scale2, float &m_run, float &l_run, f32x4 O[8], int n,
                                              int kg, BlkOf blk_of, PhysOf phys_of) {
-  int slot = slot0 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  int blk = -1, phys = -1;
-  auto next = [&]() {                            // the next valid slot at or after `slot`
-    for (; slot < slot1; slot += kAttnWaves) {
-      blk = blk_of(slot);
+  constexpr int kRanges = 8 / NT, kSpan = 16 * NT, kSlotStep = NW / kRanges;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int toff = (wave % kRanges) * kSpan;
+  int slot = slot0 + wave / kRanges;
+  int t0 = 0, phys = -1;
+  auto next = [&]() {                            // the next slot at or after `slot` with a range to attend
+    for (; slot < slot1; slot += kSlotStep) {
+      const int blk = blk_of(slot);
       if (blk < 0) continue;
+      t0 = blk * kTokens + toff;
+      if (t0 > pos) continue;
       phys = phys_of(blk);
       if (phys >= 0) return true;
     }
     return false;
   };
   if (!next()) return;
-  if (blk * kTokens + kTokens - 1 <= pos)
-    attend_block<FMT, true, true>(c, phys, blk * kTokens, pos, q, H, qk_scale2, m_run, l_run, O, n, kg);
+  if (t0 + kSpan - 1 <= pos)
+    attend_block<FMT, true, true, NT>(c, phys, toff, t0, pos, q, H, qk_scale2, m_run, l_run, O, n, kg);
   else
-    attend_block<FMT, false, true>(c, phys, blk * kTokens, pos, q, H, qk_scale2, m_run, l_run, O, n, kg);
-  slot += kAttnWaves;
+    attend_block<FMT, false, true, NT>(c, phys, toff, t0, pos, q, H, qk_scale2, m_run, l_run, O, n, kg);
+  slot += kSlotStep;
   while (next()) {
-    if (blk * kTokens + kTokens - 1 <= pos)
-      attend_block<FMT, true, false>(c, phys, blk * kTokens, pos, q, H, qk_scale2, m_run, l_run, O, n, kg);
+    if (t0 + kSpan - 1 <= pos)
+      attend_block<FMT, true, false, NT>(c, phys, toff, t0, pos, q, H, qk_scale2, m_run, l_run, O, n, kg);
     else
-      attend_block<FMT, false, false>(c, phys, blk * kTokens, pos, q, H, qk_scale2, m_run, l_run, O, n, kg);
-    slot += kAttnWaves;
+      attend_block<FMT, false, false, NT>(c, phys, toff, t0, pos, q, H, qk_scale2, m_run, l_run, O, n, kg);
+    slot += kSlotStep;
   }
 }
 
@@ -318,12 +340,14 @@ __device__ __forceinline__ void put(float *p, float v) {
     *p = v;
 }
 
-// This wave's sums for head n (m_run in log2 units), then the 4-wave merge
+// This wave's sums for head n (m_run in log2 units), then the NW-wave merge
 // through LDS into the workgroup's partial (m, l, O) of partition p; m is
-// stored in natural-log units.
-template <bool COHERENT>
-__device__ __forceinline__ void write_partial(float (&s_m)[kAttnWaves][16], float (&s_l)[kAttnWaves][16],
-                                              float (&s_o)[kAttnWaves][16][kDim + 4], float m_run, float l_run,
+// stored in natural-log units. Every wave leaves (m, l) and its unscaled O in
+// LDS at once; after the one barrier each output element is summed over the
+// waves with the factors 2^(m_w - M) (0 for a wave that saw no token).
+template <bool COHERENT, int NW>
+__device__ __forceinline__ void write_partial(float (&s_m)[NW][16], float (&s_l)[NW][16],
+                                              float (&s_o)[NW][16][kDim + 4], float m_run, float l_run,
                                               const f32x4 O[8], int row, int H, int P, int p, float *__restrict__ sp_m,
                                               float *__restrict__ sp_l, float *__restrict__ sp_o) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -335,31 +359,31 @@ __device__ __forceinline__ void write_partial(float (&s_m)[kAttnWaves][16], floa
     s_m[wave][n] = m_run;
     s_l[wave][n] = l_run;
   }
-  lds_barrier();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int h = 4 * kg + i;
-    float M = NEG_INF;
-#pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    const float mine = s_m[wave][h];
-    const float f = (mine == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(mine - M);
-    f32x4 *dst = reinterpret_cast<f32x4 *>(&s_o[wave][h][8 * n]);
-    dst[0] = f32x4{O[0][i] * f, O[1][i] * f, O[2][i] * f, O[3][i] * f};
-    dst[1] = f32x4{O[4][i] * f, O[5][i] * f, O[6][i] * f, O[7][i] * f};
+    f32x4 *dst = reinterpret_cast<f32x4 *>(&s_o[wave][4 * kg + i][8 * n]);
+    dst[0] = f32x4{O[0][i], O[1][i], O[2][i], O[3][i]};
+    dst[1] = f32x4{O[4][i], O[5][i], O[6][i], O[7][i]};
   }
   lds_barrier();
   const int64_t part = (int64_t)row * H;      // + h, then * P + p
   float *const row_o = sp_o + part * P * kDim;
   const __amdgpu_buffer_rsrc_t ro = row_rsrc(row_o, H * P * kDim);
 #pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const int idx = threadIdx.x + 256 * rr;
+  for (int rr = 0; rr < 512 / (64 * NW); ++rr) {   // 16 heads x 32 float4 of O
+    const int idx = threadIdx.x + 64 * NW * rr;
     const int h = idx >> 5, d = 4 * (idx & 31);
     if (h < H) {
-      f32x4 o = *reinterpret_cast<const f32x4 *>(&s_o[0][h][d]);
+      float M = NEG_INF;
 #pragma unroll
-      for (int w = 1; w < kAttnWaves; ++w) o += *reinterpret_cast<const f32x4 *>(&s_o[w][h][d]);
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][h]);
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = s_m[w][h];
+        const float f = (mw == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+        o += *reinterpret_cast<const f32x4 *>(&s_o[w][h][d]) * f;
+      }
       const int32_t off = (h * P + p) * kDim + d;
       if constexpr (COHERENT)
         store4_coherent(ro, off, o);
@@ -371,10 +395,10 @@ __device__ __forceinline__ void write_partial(float (&s_m)[kAttnWaves][16], floa
     const int h = threadIdx.x;
     float M = NEG_INF;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][h]);
     float Lsum = 0.f;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w)
+    for (int w = 0; w < NW; ++w)
       Lsum += (s_m[w][h] == NEG_INF) ? 0.0f : s_l[w][h] * __builtin_amdgcn_exp2f(s_m[w][h] - M);
     put<COHERENT>(sp_m + (part + h) * P + p, M * kLn2);
     put<COHERENT>(sp_l + (part + h) * P + p, Lsum);
@@ -403,7 +427,7 @@ __global__ __launch_bounds__(256) void k_split_attn(CacheView c, const void *__r
   f32x4 O[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  attend_slots<FMT>(
+  attend_slots<FMT, kAttnWaves, 8>(
       c, slot0, slot1, pos, qr, H, sm_scale * kLog2e, m_run, l_run, O, n, kg,
       [&](int slot) {
         const int blk = __builtin_amdgcn_readfirstlane(block_table[(int64_t)row * topk + slot]);
@@ -413,7 +437,7 @@ __global__ __launch_bounds__(256) void k_split_attn(CacheView c, const void *__r
         const int phys = __builtin_amdgcn_readfirstlane(c.page_table[(int64_t)b * c.stride + blk]);
         return (phys < 0 || phys >= c.num_pages) ? -1 : phys;
       });
-  write_partial<false>(s_m, s_l, s_o, m_run, l_run, O, row, H, P, p, sp_m, sp_l, sp_o);
+  write_partial<false, kAttnWaves>(s_m, s_l, s_o, m_run, l_run, O, row, H, P, p, sp_m, sp_l, sp_o);
 }
 
 // The decode step's attention. SELECT: the workgroup first selects its row's
@@ -426,16 +450,17 @@ __global__ __launch_bounds__(256) void k_split_attn(CacheView c, const void *__r
 // row or table row and the page-table row — is requested in one round trip;
 // the query goes out with the first block's pages.
 template <int FMT, int ITEMS, bool SELECT>
-__global__ __launch_bounds__(256) void k_select_attn(CacheView c, const float *__restrict__ scores,
+__global__ __launch_bounds__(64 * kStepWaves) void k_select_attn(CacheView c, const float *__restrict__ scores,
                                                      const void *__restrict__ qv, int32_t q_rows, int32_t H,
                                                      int32_t topk, int32_t P, float sm_scale,
                                                      int32_t *__restrict__ block_table, float *__restrict__ sp_m,
                                                      float *__restrict__ sp_l, float *__restrict__ sp_o,
                                                      FusedMerge fm) {
-  __shared__ TopkSmem<SELECT ? ITEMS : 1> tk;
-  __shared__ int32_t s_pt[kTopkThreads * ITEMS];
-  __shared__ float s_m[kAttnWaves][16], s_l[kAttnWaves][16];
-  __shared__ float s_o[kAttnWaves][16][kDim + 4];
+  constexpr int NT = 64 * kStepWaves;              // threads
+  __shared__ TopkSmem<SELECT ? ITEMS : 1, kStepWaves> tk;
+  __shared__ int32_t s_pt[NT * ITEMS];
+  __shared__ float s_m[kStepWaves][16], s_l[kStepWaves][16];
+  __shared__ float s_o[kStepWaves][16][kDim + 4];
   __shared__ uint32_t s_last;
   const int p = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int row = b * q_rows + j;
@@ -449,7 +474,7 @@ __global__ __launch_bounds__(256) void k_select_attn(CacheView c, const float *_
   int32_t given = -1;
 #pragma unroll
   for (int r = 0; r < ITEMS; ++r) {
-    const int i = min(tid + kTopkThreads * r, stride - 1);   // clamped: unconditional loads
+    const int i = min(tid + NT * r, stride - 1);   // clamped: unconditional loads
     if constexpr (SELECT) v[r] = scores[(int64_t)row * stride + i];
     pt[r] = c.page_table[(int64_t)b * stride + i];
   }
@@ -457,12 +482,12 @@ __global__ __launch_bounds__(256) void k_select_attn(CacheView c, const float *_
   const int pos = L - q_rows + j;
 #pragma unroll
   for (int r = 0; r < ITEMS; ++r)
-    if (tid + kTopkThreads * r < stride) s_pt[tid + kTopkThreads * r] = pt[r];
+    if (tid + NT * r < stride) s_pt[tid + NT * r] = pt[r];
   int n_sel;
   uint32_t sel;
   if constexpr (SELECT) {
     const int n_cand = pos < 0 ? 0 : min(pos / kTokens + 1, stride);
-    sel = wg_topk<ITEMS>(v, n_cand, topk, tk, n_sel);
+    sel = wg_topk<ITEMS, kStepWaves>(v, n_cand, topk, tk, n_sel);
     lds_barrier();                                 // s_pt (the selection may return before any barrier)
     if (p == 0 && tid < topk) block_table[(int64_t)row * topk + tid] = tid < n_sel ? (int32_t)sel : -1;
   } else {
@@ -479,7 +504,7 @@ __global__ __launch_bounds__(256) void k_select_attn(CacheView c, const float *_
   f32x4 O[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  attend_slots<FMT>(
+  attend_slots<FMT, kStepWaves, kStepTiles>(
       c, slot0, slot1, pos, qr, H, sm_scale * kLog2e, m_run, l_run, O, n, kg,
       [&](int slot) {
         const int blk = __builtin_amdgcn_readlane((int)sel, slot);
@@ -490,7 +515,7 @@ __global__ __launch_bounds__(256) void k_select_attn(CacheView c, const float *_
         const int phys = __builtin_amdgcn_readfirstlane(s_pt[blk]);
         return (phys < 0 || phys >= c.num_pages) ? -1 : phys;
       });
-  write_partial<true>(s_m, s_l, s_o, m_run, l_run, O, row, H, P, p, sp_m, sp_l, sp_o);
+  write_partial<true, kStepWaves>(s_m, s_l, s_o, m_run, l_run, O, row, H, P, p, sp_m, sp_l, sp_o);
 
   // ---- the row's merge, by its last partition workgroup to finish. The
   // partials went out as agent-scope (device-coherent) stores; once every
@@ -527,17 +552,19 @@ template <bool SELECT>
 static void launch_attn_items(const CacheView &c, const float *scores, const void *q, int32_t B, int32_t q_rows,
                               int32_t H, int32_t topk, int32_t P, float sm_scale, int32_t *block_table, float *sp_m,
                               float *sp_l, float *sp_o, const FusedMerge &fm, hipStream_t s) {
-  const dim3 grid((unsigned)P, (unsigned)q_rows, (unsigned)B), block(kTopkThreads);
+  constexpr int NT = 64 * kStepWaves;
+  const dim3 grid((unsigned)P, (unsigned)q_rows, (unsigned)B), block(NT);
 #define MXS_SELECT_ATTN(F, I)                                                                                   \
   hipLaunchKernelGGL((k_select_attn<F, I, SELECT>), grid, block, 0, s, c, scores, q, q_rows, H, topk, P,       \
                      sm_scale, block_table, sp_m, sp_l, sp_o, fm)
+  static_assert(NT * 32 >= MXS_MAX_PAGES_PER_SEQ, "candidates per thread");
   if (c.kv_format == 0) {
-    if (c.stride <= kTopkThreads * 2) MXS_SELECT_ATTN(0, 2);
-    else if (c.stride <= kTopkThreads * 8) MXS_SELECT_ATTN(0, 8);
+    if (c.stride <= NT * 2) MXS_SELECT_ATTN(0, 2);
+    else if (c.stride <= NT * 8) MXS_SELECT_ATTN(0, 8);
     else MXS_SELECT_ATTN(0, 32);
   } else {
-    if (c.stride <= kTopkThreads * 2) MXS_SELECT_ATTN(1, 2);
-    else if (c.stride <= kTopkThreads * 8) MXS_SELECT_ATTN(1, 8);
+    if (c.stride <= NT * 2) MXS_SELECT_ATTN(1, 2);
+    else if (c.stride <= NT * 8) MXS_SELECT_ATTN(1, 8);
     else MXS_SELECT_ATTN(1, 32);
   }
 #undef MXS_SELECT_ATTN

@@ -7,11 +7,13 @@
 
 namespace mxs {
 
+constexpr int kTopkWaves = 4, kTopkThreads = 64 * kTopkWaves;
+
 template <int ITEMS>   // candidates per thread: n_cand <= 256 * ITEMS
 __global__ __launch_bounds__(kTopkThreads) void k_topk(const float *__restrict__ scores,
                                                        const int32_t *__restrict__ context_lens, int32_t stride,
                                                        int32_t q, int32_t topk, int32_t *__restrict__ block_table) {
-  __shared__ TopkSmem<ITEMS> sm;
+  __shared__ TopkSmem<ITEMS, kTopkWaves> sm;
   const int row = blockIdx.x;
   const int b = row / q, j = row % q;
   const int tid = threadIdx.x;
@@ -24,7 +26,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float *__restrict__
   for (int r = 0; r < ITEMS; ++r) v[r] = s[min(tid + kTopkThreads * r, stride - 1)];
   const int n_cand = pos < 0 ? 0 : min(pos / kTokens + 1, (int)stride);
   int n_sel;
-  const uint32_t sel = wg_topk<ITEMS>(v, n_cand, topk, sm, n_sel);
+  const uint32_t sel = wg_topk<ITEMS, kTopkWaves>(v, n_cand, topk, sm, n_sel);
   if (tid < topk) block_table[(int64_t)row * topk + tid] = tid < n_sel ? (int32_t)sel : -1;
 }
 

@@ -1,4 +1,5 @@
-// Exact top-k block selection of one query row by one 256-thread workgroup.
+// Exact top-k block selection of one query row by one workgroup of 4 or 8
+// waves (NT = 256 or 512 threads).
 //
 // ATOM PR #2686 ("Enable Mono decode with fixed DSpark verify", the review
 // thread's commit message: each sparse layer selects its own sparse blocks)
@@ -10,13 +11,14 @@
 // kernel, which selects its row's blocks itself before attending to them.
 //
 // Keys are the scores mapped to order-preserving uint32 (NaN ranks lowest).
-// Thread t holds candidates t + 256 r. Steps:
-//   1. T0 = the k-th largest of the 256 thread maxima, a lower bound of the
+// Thread t holds candidates t + NT r. Steps:
+//   1. T0 = the k-th largest of the NT thread maxima, a lower bound of the
 //      k-th largest score (k threads each hold a score >= T0): every wave
-//      sorts its 64 maxima, and each wave merges the four sorted lists itself
-//      (bitonic half-cleaners), so no wave waits for another beyond one barrier;
+//      sorts its 64 maxima, and each wave merges the sorted lists of all waves
+//      itself (bitonic half-cleaners, keeping the top 64 of each pair), so no
+//      wave waits for another beyond one barrier;
 //   2. every candidate with key >= T0 (typically a few dozen) is compacted
-//      into LDS in ascending id order (id = tid + 256 r ascends with (r, wave,
+//      into LDS in ascending id order (id = tid + NT r ascends with (r, wave,
 //      lane): per-(r, wave) ballot counts, one barrier for the counts);
 //   3. exactly k survivors are the selection, already ascending; when at most
 //      64 survive, every wave holds them one per lane, finds the k-th largest
@@ -30,8 +32,6 @@
 #include "common.hpp"
 
 namespace mxs {
-
-constexpr int kTopkThreads = 256;
 
 __device__ __forceinline__ uint32_t order_key(float f) {        // branch-free
   const uint32_t u = f2u(f);
@@ -80,23 +80,40 @@ __device__ __forceinline__ uint32_t merge64(uint32_t v) {
 // every global load still in flight).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int ITEMS>
+template <int ITEMS, int NW = 4>
 struct TopkSmem {
-  uint32_t key[kTopkThreads * ITEMS];      // survivors, ascending id
-  uint16_t idx[kTopkThreads * ITEMS];
-  uint32_t wmax[4][64];                    // each wave's thread maxima, sorted descending
-  alignas(16) uint32_t wcnt[ITEMS][4];     // survivors of item r in wave w (read 16 B at a time)
+  static constexpr int kThreads = 64 * NW;
+  uint32_t key[kThreads * ITEMS];          // survivors, ascending id
+  uint16_t idx[kThreads * ITEMS];
+  uint32_t wmax[NW][64];                   // each wave's thread maxima, sorted descending
+  alignas(16) uint32_t wcnt[ITEMS][NW];    // survivors of item r in wave w (read 16 B at a time)
   uint32_t by_rank[64];                    // many-survivor path: id of rank r
 };
 
-// Selects the top-k of one row; every thread of the 256 calls it. Thread t
-// passes the scores of candidates t + 256 r in v[r] (any value where
-// t + 256 r >= n_cand), 0 <= n_cand <= 256 ITEMS, 1 <= topk <= 64. Every wave
+// The top 64 of the sorted (descending) lists of waves [W0, W0 + N), sorted
+// DESC (or ascending): pairs of lists are merged with a bitonic half-cleaner
+// that keeps the larger half.
+template <bool DESC, int W0, int N, int NW>
+__device__ __forceinline__ uint32_t top64_of_waves(const uint32_t (&wmax)[NW][64], int lane) {
+  if constexpr (N == 1) {
+    return DESC ? wmax[W0][lane] : wmax[W0][63 - lane];
+  } else {
+    const uint32_t a = top64_of_waves<true, W0, N / 2, NW>(wmax, lane);        // descending
+    const uint32_t b = top64_of_waves<false, W0 + N / 2, N / 2, NW>(wmax, lane);  // ascending
+    return merge64<DESC>(max(a, b));
+  }
+}
+
+// Selects the top-k of one row; every thread of the workgroup calls it.
+// Thread t passes the scores of candidates t + NT r in v[r] (any value where
+// t + NT r >= n_cand), 0 <= n_cand <= NT ITEMS, 1 <= topk <= 64. Every wave
 // gets back, in lane s < n_sel = min(topk, n_cand), the s-th smallest selected
 // block id (other lanes: 0xFFFFFFFF, or the lane number when n_cand <= topk).
-template <int ITEMS>
-__device__ __forceinline__ uint32_t wg_topk(const float (&v)[ITEMS], int n_cand, int topk, TopkSmem<ITEMS> &sm,
+template <int ITEMS, int NW>
+__device__ __forceinline__ uint32_t wg_topk(const float (&v)[ITEMS], int n_cand, int topk, TopkSmem<ITEMS, NW> &sm,
                                             int &n_sel) {
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  constexpr int NT = 64 * NW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (n_cand <= topk) {                      // every candidate is selected
     n_sel = n_cand;
@@ -107,15 +124,13 @@ __device__ __forceinline__ uint32_t wg_topk(const float (&v)[ITEMS], int n_cand,
   uint32_t m = 0u;
 #pragma unroll
   for (int r = 0; r < ITEMS; ++r) {
-    key[r] = tid + kTopkThreads * r < n_cand ? order_key(v[r]) : 0u;
+    key[r] = tid + NT * r < n_cand ? order_key(v[r]) : 0u;
     m = max(m, key[r]);
   }
-  // 1. T0: the k-th largest of the 256 thread maxima
+  // 1. T0: the k-th largest of the NT thread maxima
   sm.wmax[wave][lane] = sort64<true>(m);
   lds_barrier();
-  const uint32_t c = merge64<true>(max(sm.wmax[0][lane], sm.wmax[1][63 - lane]));   // top 64 of waves 0, 1
-  const uint32_t d = merge64<false>(max(sm.wmax[2][lane], sm.wmax[3][63 - lane]));  // of waves 2, 3, ascending
-  const uint32_t e = merge64<true>(max(c, d));                                        // of all four
+  const uint32_t e = top64_of_waves<true, 0, NW, NW>(sm.wmax, lane);
   const uint32_t T0 = (uint32_t)__builtin_amdgcn_readlane((int)e, topk - 1);
 
   // 2. compact the survivors in ascending id order: item r of wave w lands
@@ -124,7 +139,7 @@ __device__ __forceinline__ uint32_t wg_topk(const float (&v)[ITEMS], int n_cand,
   uint32_t at[ITEMS];
 #pragma unroll
   for (int r = 0; r < ITEMS; ++r) {
-    keep[r] = tid + kTopkThreads * r < n_cand && key[r] >= T0;
+    keep[r] = tid + NT * r < n_cand && key[r] >= T0;
     const uint64_t bal = __ballot(keep[r]);
     at[r] = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
     if (lane == 0) sm.wcnt[r][wave] = (uint32_t)__popcll(bal);
@@ -133,12 +148,21 @@ __device__ __forceinline__ uint32_t wg_topk(const float (&v)[ITEMS], int n_cand,
   uint32_t n_surv = 0;
 #pragma unroll
   for (int r = 0; r < ITEMS; ++r) {
-    const u32x4 c = *reinterpret_cast<const u32x4 *>(sm.wcnt[r]);
-    const uint32_t base = n_surv + (wave > 0 ? c[0] : 0u) + (wave > 1 ? c[1] : 0u) + (wave > 2 ? c[2] : 0u);
-    n_surv += c[0] + c[1] + c[2] + c[3];
+    uint32_t below = 0, all = 0;
+#pragma unroll
+    for (int w4 = 0; w4 < NW; w4 += 4) {
+      const u32x4 c = *reinterpret_cast<const u32x4 *>(&sm.wcnt[r][w4]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        below += wave > w4 + i ? c[i] : 0u;
+        all += c[i];
+      }
+    }
+    const uint32_t base = n_surv + below;
+    n_surv += all;
     if (keep[r]) {
       sm.key[base + at[r]] = key[r];
-      sm.idx[base + at[r]] = (uint16_t)(tid + kTopkThreads * r);
+      sm.idx[base + at[r]] = (uint16_t)(tid + NT * r);
     }
   }
   lds_barrier();
@@ -162,7 +186,7 @@ __device__ __forceinline__ uint32_t wg_topk(const float (&v)[ITEMS], int n_cand,
     return lane < topk ? got : 0xFFFFFFFFu;
   }
   // ties at the bound: rank through LDS, then sort the selected ids
-  for (uint32_t i = tid; i < n_surv; i += kTopkThreads) {
+  for (uint32_t i = tid; i < n_surv; i += NT) {
     const uint32_t ki = sm.key[i], ii = sm.idx[i];
     uint32_t rank = 0;
     for (uint32_t o = 0; o < n_surv; ++o) {
