@@ -181,6 +181,10 @@ int sparse_split_attn(const mxs_cache *cache, const void *q, int32_t q_dtype,
                       const int32_t *block_table, int32_t B, int32_t q_rows, int32_t H,
                       int32_t topk, int32_t num_partitions, float sm_scale, float *sp_m,
                       float *sp_l, float *sp_o, void *stream);
+/* The partition count the library takes for num_partitions = 0:
+ * min(ceil(topk / 4), max(1, 256 / (B q_rows))), clamped to 1..64 — one block
+ * per wave of a 4-wave workgroup, but no more workgroups than MI355X has CUs
+ * once the rows alone fill it (a choice of this library; the pages fix none). */
 int mxs_default_partitions(int32_t B, int32_t q_rows, int32_t topk);
 
 /* ---- 6. merge ------------------------------------------------------------

@@ -4,6 +4,7 @@
 // work was launched.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -90,9 +91,18 @@ mxs::CacheView view(const mxs_cache *c) {
 
 size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
 
-int default_partitions(int32_t topk) {
-  int p = (topk + 3) / 4;   // one block per wave of a 4-wave partition
-  return p < 1 ? 1 : (p > MXS_MAX_PARTITIONS ? MXS_MAX_PARTITIONS : p);
+// Partitions per query row when the caller leaves the choice to the library:
+// one block per wave of a 4-wave partition workgroup (ceil(topk / 4)), but no
+// more than it takes to give each of MI355X's 256 CUs one workgroup. Every
+// workgroup runs the same dependent chain (selection, block loads, exchange of
+// partials), so when the rows alone fill the GPU, fewer and longer partitions
+// beat several rounds of short ones.
+constexpr int64_t kTargetWorkgroups = 256;
+int default_partitions(int32_t B, int32_t q_rows, int32_t topk) {
+  const int64_t rows = (int64_t)B * q_rows;
+  int64_t p = (topk + 3) / 4;
+  if (rows > 0) p = std::min<int64_t>(p, std::max<int64_t>(1, kTargetWorkgroups / rows));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(p, MXS_MAX_PARTITIONS));
 }
 
 // workspace segments of decode_step, in order
@@ -231,9 +241,7 @@ int index_score_topk(const mxs_cache *cache, const uint16_t *q_idx, const float 
 }
 
 int mxs_default_partitions(int32_t B, int32_t q_rows, int32_t topk) {
-  (void)B;
-  (void)q_rows;
-  return default_partitions(topk);
+  return default_partitions(B, q_rows, topk);
 }
 
 static int check_attn_args(const mxs_cache *cache, const void *q, int32_t q_dtype, const int32_t *block_table,
@@ -258,7 +266,7 @@ static int check_attn_args(const mxs_cache *cache, const void *q, int32_t q_dtyp
 int sparse_split_attn(const mxs_cache *cache, const void *q, int32_t q_dtype, const int32_t *block_table, int32_t B,
                       int32_t q_rows, int32_t H, int32_t topk, int32_t num_partitions, float sm_scale, float *sp_m,
                       float *sp_l, float *sp_o, void *stream) {
-  const int32_t P = num_partitions == 0 ? default_partitions(topk) : num_partitions;
+  const int32_t P = num_partitions == 0 ? default_partitions(B, q_rows, topk) : num_partitions;
   if (int r = check_attn_args(cache, q, q_dtype, block_table, B, q_rows, H, topk, P, sm_scale)) return r;
   REQ(sp_m && sp_l && sp_o, MXS_EINVAL, "sp_m / sp_l / sp_o: null");
   REQ(aligned(sp_m, 4) && aligned(sp_l, 4) && aligned(sp_o, 16), MXS_EINVAL, "sp_m / sp_l / sp_o: misaligned");
@@ -285,7 +293,7 @@ size_t mxs_workspace_bytes(int32_t B, int32_t q, int32_t H, int32_t H_I, int32_t
                            int32_t num_partitions) {
   (void)H_I;
   if (B < 0 || q < 0 || H < 0 || topk < 0 || page_table_stride < 0) return 0;
-  const int32_t P = num_partitions == 0 ? default_partitions(topk) : num_partitions;
+  const int32_t P = num_partitions == 0 ? default_partitions(B, q, topk) : num_partitions;
   return step_ws(B, q, H, topk, page_table_stride, P).total;
 }
 
@@ -296,7 +304,7 @@ int decode_step(const mxs_step *a, void *ws, size_t ws_bytes, void *stream) {
   if (int r = check_rows(a->B, a->q)) return r;
   if (int r = check_topk(a->topk)) return r;
   if (a->B == 0) return ok();                      // an empty batch: nothing to do
-  const int32_t P = a->num_partitions == 0 ? default_partitions(a->topk) : a->num_partitions;
+  const int32_t P = a->num_partitions == 0 ? default_partitions(a->B, a->q, a->topk) : a->num_partitions;
   const bool mx = cache->kv_format == MXS_FMT_MXFP4;
   if (mx)
     REQ(a->q_dtype == MXS_F32 || a->q_dtype == MXS_BF16, MXS_EUNSUPPORTED,
@@ -375,7 +383,7 @@ int decode_step_reuse(const mxs_step *a, const int32_t *block_table, void *ws, s
   if (int r = check_rows(a->B, a->q)) return r;
   if (int r = check_topk(a->topk)) return r;
   if (a->B == 0) return ok();                      // an empty batch: nothing to do
-  const int32_t P = a->num_partitions == 0 ? default_partitions(a->topk) : a->num_partitions;
+  const int32_t P = a->num_partitions == 0 ? default_partitions(a->B, a->q, a->topk) : a->num_partitions;
   const bool mx = cache->kv_format == MXS_FMT_MXFP4;
   if (mx)
     REQ(a->q_dtype == MXS_F32 || a->q_dtype == MXS_BF16, MXS_EUNSUPPORTED,

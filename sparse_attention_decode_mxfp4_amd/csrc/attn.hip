@@ -340,19 +340,16 @@ __device__ __forceinline__ void put(float *p, float v) {
     *p = v;
 }
 
-// This wave's sums for head n (m_run in log2 units), then the NW-wave merge
-// through LDS into the workgroup's partial (m, l, O) of partition p; m is
-// stored in natural-log units. Every wave leaves (m, l) and its unscaled O in
-// LDS at once; after the one barrier each output element is summed over the
+// This wave's sums for head n (m_run in log2 units) into LDS for the NW-wave
+// merge: every wave leaves (m, l) and its unscaled O at once, then the one
+// barrier; the merged value of each output element is then the sum over the
 // waves with the factors 2^(m_w - M) (0 for a wave that saw no token).
-template <bool COHERENT, int NW>
-__device__ __forceinline__ void write_partial(float (&s_m)[NW][16], float (&s_l)[NW][16],
-                                              float (&s_o)[NW][16][kDim + 4], float m_run, float l_run,
-                                              const f32x4 O[8], int row, int H, int P, int p, float *__restrict__ sp_m,
-                                              float *__restrict__ sp_l, float *__restrict__ sp_o) {
+template <int NW>
+__device__ __forceinline__ void stage_waves(float (&s_m)[NW][16], float (&s_l)[NW][16],
+                                            float (&s_o)[NW][16][kDim + 4], float m_run, float l_run,
+                                            const f32x4 O[8]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, kg = lane >> 4;
-  const float NEG_INF = -__builtin_inff();
   l_run += u2f(xor_lane<16>(f2u(l_run)));
   l_run += u2f(xor_lane<32>(f2u(l_run)));
   if (kg == 0) {
@@ -366,6 +363,38 @@ __device__ __forceinline__ void write_partial(float (&s_m)[NW][16], float (&s_l)
     dst[1] = f32x4{O[4][i], O[5][i], O[6][i], O[7][i]};
   }
   lds_barrier();
+}
+
+// Head h's merged M (log2 units), the waves' factors folded into O's 4
+// elements d .. d + 3, and (LSUM) the merged l.
+template <int NW, bool LSUM>
+__device__ __forceinline__ f32x4 merged(const float (&s_m)[NW][16], const float (&s_l)[NW][16],
+                                        const float (&s_o)[NW][16][kDim + 4], int h, int d, float &M, float &Lsum) {
+  const float NEG_INF = -__builtin_inff();
+  M = NEG_INF;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][h]);
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  Lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const float mw = s_m[w][h];
+    const float f = (mw == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+    o += *reinterpret_cast<const f32x4 *>(&s_o[w][h][d]) * f;
+    if constexpr (LSUM) Lsum += (mw == NEG_INF) ? 0.0f : s_l[w][h] * f;
+  }
+  return o;
+}
+
+// The workgroup's partial (m, l, O) of partition p from the staged waves; m is
+// stored in natural-log units.
+template <bool COHERENT, int NW>
+__device__ __forceinline__ void write_partial(float (&s_m)[NW][16], float (&s_l)[NW][16],
+                                              float (&s_o)[NW][16][kDim + 4], float m_run, float l_run,
+                                              const f32x4 O[8], int row, int H, int P, int p, float *__restrict__ sp_m,
+                                              float *__restrict__ sp_l, float *__restrict__ sp_o) {
+  const float NEG_INF = -__builtin_inff();
+  stage_waves<NW>(s_m, s_l, s_o, m_run, l_run, O);
   const int64_t part = (int64_t)row * H;      // + h, then * P + p
   float *const row_o = sp_o + part * P * kDim;
   const __amdgpu_buffer_rsrc_t ro = row_rsrc(row_o, H * P * kDim);
@@ -374,16 +403,8 @@ __device__ __forceinline__ void write_partial(float (&s_m)[NW][16], float (&s_l)
     const int idx = threadIdx.x + 64 * NW * rr;
     const int h = idx >> 5, d = 4 * (idx & 31);
     if (h < H) {
-      float M = NEG_INF;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][h]);
-      f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float mw = s_m[w][h];
-        const float f = (mw == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-        o += *reinterpret_cast<const f32x4 *>(&s_o[w][h][d]) * f;
-      }
+      float M, unused;
+      const f32x4 o = merged<NW, false>(s_m, s_l, s_o, h, d, M, unused);
       const int32_t off = (h * P + p) * kDim + d;
       if constexpr (COHERENT)
         store4_coherent(ro, off, o);
@@ -402,6 +423,38 @@ __device__ __forceinline__ void write_partial(float (&s_m)[NW][16], float (&s_l)
       Lsum += (s_m[w][h] == NEG_INF) ? 0.0f : s_l[w][h] * __builtin_amdgcn_exp2f(s_m[w][h] - M);
     put<COHERENT>(sp_m + (part + h) * P + p, M * kLn2);
     put<COHERENT>(sp_l + (part + h) * P + p, Lsum);
+  }
+}
+
+// A row attended by one partition: the staged waves merged straight into the
+// row's output (O / l as bf16, lse = m + ln l), the same values the merge of a
+// single partition gives (its weight is exactly 1).
+template <int NW>
+__device__ __forceinline__ void write_row(float (&s_m)[NW][16], float (&s_l)[NW][16], float (&s_o)[NW][16][kDim + 4],
+                                          float m_run, float l_run, const f32x4 O[8], int row, int H,
+                                          uint16_t *__restrict__ out, float *__restrict__ lse) {
+  stage_waves<NW>(s_m, s_l, s_o, m_run, l_run, O);
+#pragma unroll
+  for (int rr = 0; rr < 512 / (64 * NW); ++rr) {   // 16 heads x 32 groups of 4 elements
+    const int idx = threadIdx.x + 64 * NW * rr;
+    const int h = idx >> 5, d = 4 * (idx & 31);
+    if (h < H) {
+      float M, Lsum;
+      const f32x4 o = merged<NW, true>(s_m, s_l, s_o, h, d, M, Lsum);
+      const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+      const int64_t r = (int64_t)row * H + h;
+      uint2 packed;
+      packed.x = bf16_pair(o[0] * inv, o[1] * inv);
+      packed.y = bf16_pair(o[2] * inv, o[3] * inv);
+      uint16_t *const dst = out + r * kDim + d;                      // out: at least 4-byte aligned
+      if ((reinterpret_cast<uintptr_t>(out) & 7) == 0) {
+        *reinterpret_cast<uint2 *>(dst) = packed;
+      } else {
+        reinterpret_cast<uint32_t *>(dst)[0] = packed.x;
+        reinterpret_cast<uint32_t *>(dst)[1] = packed.y;
+      }
+      if (lse && d == 0) lse[r] = Lsum > 0.0f ? M * kLn2 + __logf(Lsum) : -__builtin_inff();
+    }
   }
 }
 
@@ -515,6 +568,10 @@ __global__ __launch_bounds__(64 * kStepWaves) void k_select_attn(CacheView c, co
         const int phys = __builtin_amdgcn_readfirstlane(s_pt[blk]);
         return (phys < 0 || phys >= c.num_pages) ? -1 : phys;
       });
+  if (P == 1) {                                     // the row is this workgroup's alone: no exchange
+    write_row<kStepWaves>(s_m, s_l, s_o, m_run, l_run, O, row, H, fm.out, fm.lse);
+    return;
+  }
   write_partial<true, kStepWaves>(s_m, s_l, s_o, m_run, l_run, O, row, H, P, p, sp_m, sp_l, sp_o);
 
   // ---- the row's merge, by its last partition workgroup to finish. The

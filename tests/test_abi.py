@@ -52,6 +52,11 @@ def test_workspace_sizes(L):
     assert L.mxs_default_partitions(4, 8, 32) == 8
     assert L.mxs_default_partitions(1, 1, 4) == 1
     assert L.mxs_default_partitions(1, 1, 1000) == 64
+    # once the rows alone fill the GPU's 256 CUs, fewer (longer) partitions
+    assert L.mxs_default_partitions(4, 4, 16) == 4
+    assert L.mxs_default_partitions(16, 8, 32) == 2
+    assert L.mxs_default_partitions(32, 8, 32) == 1
+    assert L.mxs_default_partitions(64, 16, 64) == 1
     ws = L.mxs_workspace_bytes(4, 8, 16, 4, 32, 2048, 0)
     rows, P = 32, 8
     need = rows * 2048 * 4 + rows * 32 * 4 + rows * 16 * 128 + 2 * rows * 16 * P * 4 + rows * 16 * P * 128 * 4
