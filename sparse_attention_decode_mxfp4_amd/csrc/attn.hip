@@ -11,11 +11,11 @@
 // * Workgroup = (partition p, query row j, sequence b), 4 waves. Partition p
 //   owns block-table slots [p c, min((p+1) c, topk)), c = ceil(topk / P); wave
 //   w takes every 4th of them, keeps an online softmax (m, l, O) for the 16
-//   heads, and the 4 waves merge through LDS into one partial. (The block
-//   code also takes a wave's share as half a block, for a workgroup of 8
-//   waves in pairs; measured on MI355X that made the step's launch slower:
-//   the 8-wave selection and merge lose more at their barriers than the
-//   halved block work gains.)
+//   heads, and the 4 waves merge through LDS into one partial. The block code
+//   takes the wave's token range as a parameter; only whole blocks are built.
+//   (Half blocks for 8-wave workgroups, waves in pairs, measured slower on
+//   MI355X: the 8-wave selection and merge lose more at their barriers than
+//   the halved block work gains.)
 // * QK: D[token][head] = K[token][:] . q[head][:] on v_mfma_f32_16x16x32_bf16.
 //   Lane 16 kg + n loads token n's group kg — 16 bytes and one scale byte, the
 //   same coalesced pattern as the index scorer — and widens it to bf16 with

@@ -317,13 +317,24 @@ __global__ __launch_bounds__(64 * NW) void k_index_score(CacheView c, const uint
   }
   SideWork sw;
   side_prefetch(st, b, q, gw, lane, sw);
-  // the step's new index rows, requested by every wave (16 KiB per sequence,
-  // L2-resident); only the wave that holds their positions keeps them
-  float2 xr[4 * MT];
+  // The step's new index rows are quantized by the waves of the workgroup
+  // that holds their positions (rows j = wave + NW k each, into LDS; every
+  // wave of it, on either path below, so the barrier sees all of them). That
+  // workgroup is known once L (a scalar load, back well before the vector
+  // loads above) arrives; only its waves request the rows, so the other
+  // workgroups never wait for them.
+  const int wg_p0 = (n_waves - NW * (blockIdx.y + 1)) * PPW;          // the workgroup's first page
+  const bool own_wg = st.idx_new != nullptr && L >= 1 && L - 1 >= wg_p0 * kTokens &&
+                      max(L - q, 0) < (wg_p0 + NW * PPW) * kTokens;     // uniform over the workgroup
+  constexpr int kOwnRows = (4 * MT + NW - 1) / NW;
+  float2 xr[kOwnRows];
+  if (own_wg) {
 #pragma unroll
-  for (int j = 0; j < 4 * MT; ++j)
-    xr[j] = st.idx_new ? reinterpret_cast<const float2 *>(st.idx_new + ((int64_t)b * q + min(j, q - 1)) * kDim)[lane]
-                       : make_float2(0.f, 0.f);
+    for (int k = 0; k < kOwnRows; ++k)
+      xr[k] = reinterpret_cast<const float2 *>(st.idx_new + ((int64_t)b * q + min(wave + NW * k, q - 1)) * kDim)[lane];
+#pragma unroll
+    for (int k = 0; k < kOwnRows; ++k) asm volatile("" ::"v"(xr[k].x), "v"(xr[k].y));
+  }
   // Consume every prologue load here, so that no compiler-placed wait for them
   // lands inside the chunk pipeline (the compiler does not count the
   // direct-to-LDS copies and would wait for all of them).
@@ -336,24 +347,17 @@ __global__ __launch_bounds__(64 * NW) void k_index_score(CacheView c, const uint
   }
   asm volatile("" ::"v"(praw));
   asm volatile("" ::"v"(sw.row.x), "v"(sw.row.y), "v"(sw.qe));
-#pragma unroll
-  for (int j = 0; j < 4 * MT; ++j) asm volatile("" ::"v"(xr[j].x), "v"(xr[j].y));
   asm volatile("" ::"s"(L) : "memory");
 
   const int lim = min((L + kTokens - 1) / kTokens, (int)c.stride);    // pages holding tokens
-  // The step's new index rows are quantized by the waves of the workgroup
-  // that holds their positions (rows j = wave, wave + NW, ... each, into LDS;
-  // every wave of it, on either path below, so the barrier sees all of them).
-  const int wg_p0 = (n_waves - NW * (blockIdx.y + 1)) * PPW;          // the workgroup's first page
-  const bool own_wg = st.idx_new != nullptr && L >= 1 && L - 1 >= wg_p0 * kTokens &&
-                      max(L - q, 0) < (wg_p0 + NW * PPW) * kTokens;     // uniform over the workgroup
   auto quant_share = [&]() {
     if (!own_wg) return;
 #pragma unroll
-    for (int j = 0; j < 4 * MT; ++j) {
-      if (j % NW != wave) continue;
+    for (int k = 0; k < kOwnRows; ++k) {
+      const int j = wave + NW * k;
+      if (j >= 4 * MT) continue;
       uint32_t code, gsb, word;
-      quant_row<FMT>(xr[j], code, gsb, word);
+      quant_row<FMT>(xr[k], code, gsb, word);
       s_qc[64 * j + lane] = code;
       if (lane == 0) s_qw[j] = word;
     }
