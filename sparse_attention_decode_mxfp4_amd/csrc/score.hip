@@ -274,8 +274,6 @@ __global__ __launch_bounds__(64 * NW) void k_index_score(CacheView c, const uint
   const int n_waves = gridDim.y * NW, d = blockIdx.y * NW + wave;
   const int gw = (d + n_waves - 1) % n_waves;        // side-store index: d = 1, 2, ... first
   const int p0 = (n_waves - 1 - d) * PPW;
-  if (st.counters && blockIdx.y == gridDim.y - 1)   // the attention launch's merge counters for sequence b
-    for (int i = threadIdx.x; i < q; i += 64 * NW) st.counters[b * q + i] = 0u;
   const float NEG_INF = -__builtin_inff();
   float *srow = scores + (int64_t)b * q * c.stride;
 
@@ -464,6 +462,10 @@ __global__ __launch_bounds__(64 * NW) void k_index_score(CacheView c, const uint
     }
   }
   side_finish(c, st, b, q, L, gw, n_waves, lane, sw);
+  // the attention launch's merge counters for sequence b (at the end: in the
+  // prologue this would split the kernel-argument loads into two round trips)
+  if (st.counters && blockIdx.y == gridDim.y - 1)
+    for (int i = threadIdx.x; i < q; i += 64 * NW) st.counters[b * q + i] = 0u;
 }
 
 template <int FMT, int MT, class SH>
