@@ -80,16 +80,26 @@ __device__ __forceinline__ float load_q_elem(const void *q, int q_dtype, int64_t
   return reinterpret_cast<const float *>(q)[i];
 }
 
-// Four consecutive elements per thread.
+// Four consecutive elements per thread, all requested before any is used
+// (the dtype branch outside the element loop).
 __device__ __forceinline__ void pack_q4(const void *q, int q_dtype, int64_t n, uint8_t *q8, int64_t i) {
   if (i >= n) return;
-  if (i + 4 <= n && ((reinterpret_cast<uintptr_t>(q8) + i) & 3) == 0) {
-    uint32_t w = 0;
+  const int m = (int)min<int64_t>(4, n - i);
+  float v[4];
+  if (q_dtype == 1) {
+    const uint16_t *p = reinterpret_cast<const uint16_t *>(q) + i;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w |= e4m3_code(load_q_elem(q, q_dtype, i + e)) << (8 * e);
-    *reinterpret_cast<uint32_t *>(q8 + i) = w;
+    for (int e = 0; e < 4; ++e) v[e] = e < m ? u2f((uint32_t)p[e] << 16) : 0.0f;
   } else {
-    for (int e = 0; e < 4 && i + e < n; ++e) q8[i + e] = (uint8_t)e4m3_code(load_q_elem(q, q_dtype, i + e));
+    const float *p = reinterpret_cast<const float *>(q) + i;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = e < m ? p[e] : 0.0f;
+  }
+  if (m == 4 && ((reinterpret_cast<uintptr_t>(q8) + i) & 3) == 0) {
+    *reinterpret_cast<uint32_t *>(q8 + i) =
+        e4m3_code(v[0]) | (e4m3_code(v[1]) << 8) | (e4m3_code(v[2]) << 16) | (e4m3_code(v[3]) << 24);
+  } else {
+    for (int e = 0; e < m; ++e) q8[i + e] = (uint8_t)e4m3_code(v[e]);
   }
 }
 
