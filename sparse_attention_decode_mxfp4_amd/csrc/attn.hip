@@ -587,6 +587,7 @@ __global__ __launch_bounds__(64 * kStepWaves) void k_select_attn(CacheView c, co
              (uint32_t)(P - 1);
   lds_barrier();
   if (!s_last) return;
+  if (tid == 0) fm.counters[row] = 0u;            // every arrival is in: the row's counter is free for the next launch
   merge_row(sp_m, sp_l, sp_o, row, H, P, fm.out, fm.lse);
 }
 

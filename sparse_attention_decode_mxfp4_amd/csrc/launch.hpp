@@ -54,7 +54,7 @@ hipError_t launch_split_attn(const CacheView &c, const void *q, int q_dtype,
 // top-k blocks from the scores [B][q_rows][stride] itself, writes the row's
 // block table (partition 0) and attends to its partition's slots; the row's
 // last partition to finish merges the row into out / lse (counters [B][q_rows]
-// zero on entry: the scorer launch clears them)
+// zero on entry; the merging workgroup sets its row's counter back to zero)
 struct FusedMerge {
   uint32_t *counters = nullptr;
   uint16_t *out = nullptr;
