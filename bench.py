@@ -18,8 +18,9 @@ Cache), so the index scan streams from HBM, not from the MALL; the one-replica
 Prints one JSON line (rank 0): the metric (query rows/s), the whole step's
 algorithmic HBM bytes and GB/s, the roofline of the dominant kernel (the index
 scorer: 100 back-to-back launches over rotating replicas captured in one HIP
-graph, timed with HIP events on the stream they run on) and the oracle's
-throughput on a bounded sample on the host cores.
+graph, timed with HIP events on the stream they run on, beside a plain
+streaming read of the same pages, its ceiling) and the oracle's throughput on
+a bounded sample on the host cores (all of them, and one thread).
 """
 from __future__ import annotations
 
@@ -107,8 +108,9 @@ def copy_calibration(n_bytes: int = 256 << 20, reps: int = 20):
 def cpu_baseline(inp, min_seconds=10.0, max_seconds=30.0) -> dict:
     """The oracle (NumPy, float64) on sequence 0 of the workload: its whole
     decode step (row store of the new rows, scores over every page, top-k,
-    attention), repeated until at least ``min_seconds`` of CPU work."""
-    from threadpoolctl import threadpool_info
+    attention), repeated until at least ``min_seconds`` of CPU work, then once
+    more on one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import step as OS
     wl = inp.wl
     fmts = {"k": wl.kv_format, "v": wl.kv_format, "idx": wl.idx_format}
@@ -121,9 +123,14 @@ def cpu_baseline(inp, min_seconds=10.0, max_seconds=30.0) -> dict:
         if el >= min_seconds or el + el / reps > max_seconds:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    with threadpool_limits(1):                 # the same step on one thread, once
+        t1 = time.perf_counter()
+        OS.decode_step_ref(inp, pools=pools, seqs=[0])
+        el1 = time.perf_counter() - t1
     return {"value": reps * wl.q / el, "unit": "query rows/s", "cores": int(threads), "kind": "oracle",
+            "one_thread_value": wl.q / el1,
             "sample": f"sequence 0 of {wl.B} ({wl.q} query rows, {int(inp.contexts[0])}-token context): the "
-                      f"oracle's full step for that sequence, {reps} run(s) in {el:.1f} s; "
+                      f"oracle's full step for that sequence, {reps} run(s) in {el:.1f} s (one thread: one run in {el1:.1f} s); "
                       f"host affinity {len(os.sched_getaffinity(0))} cores"}
 
 
@@ -252,6 +259,26 @@ def main():
     score_bytes = ab["index_pages"] + ab["n_index_pages"] * wl.q * 4 + wl.B * wl.q * wl.H_I * (256 + 4)
     score_gbps = score_bytes / (score_us * 1e-6) / 1e9
 
+    # ---- the scan's streaming-read ceiling: the same index pages, read in the
+    # same page-table order with plain loads and no arithmetic
+    # (mxs_read_index_pages), timed the same way as the scorer
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for i in range(R):
+        mx.read_index_pages(caches[i], wl.B, sink)
+    torch.cuda.synchronize()
+    gread = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gread):
+        for i in range(n_launch):
+            mx.read_index_pages(caches[i % R], wl.B, sink)
+    gread.replay()
+    torch.cuda.synchronize()
+    ev0.record()
+    gread.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    read_us = ev0.elapsed_time(ev1) * 1e3 / n_launch
+    read_gbps = ab["index_pages"] / (read_us * 1e-6) / 1e9
+
     # ---- the step of a layer that reuses a block selection (decode_step_reuse
     # over the tables the full steps wrote): its K / V row store and query
     # store, split attention over the selected pages and the merge; R
@@ -309,7 +336,12 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "index scorer (k_index_score)", "achieved": score_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": score_gbps / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(wl.name), "avg_launch_us": score_us,
-                     "algorithmic_bytes_per_launch": score_bytes},
+                     "algorithmic_bytes_per_launch": score_bytes,
+                     "read_ceiling": {"what": "plain streaming read of the same index pages in page-table order "
+                                              "(mxs_read_index_pages), timed like the scorer",
+                                      "avg_launch_us": read_us, "GBps": read_gbps,
+                                      "frac_of_peak": read_gbps / HBM_PEAK_GBPS,
+                                      "scorer_frac_of_ceiling": score_gbps / read_gbps}},
     }
     out["attention_only_step"] = {
         "what": "decode_step_reuse: the step of a layer reusing a block selection (K/V row store, q store, "
@@ -320,7 +352,8 @@ def main():
     }
     log(f"[bench] attention-only step {reuse_us:.1f} us = {reuse_gbps:.0f} GB/s")
     log(f"[bench] step {ms_step * 1e3:.1f} us (events {ev_ms_step * 1e3:.1f} us, warm {warm_ms * 1e3:.1f} us), "
-        f"{step_gbps:.0f} GB/s; scorer {score_us:.1f} us = {score_gbps:.0f} GB/s")
+        f"{step_gbps:.0f} GB/s; scorer {score_us:.1f} us = {score_gbps:.0f} GB/s; "
+        f"read ceiling {read_us:.1f} us = {read_gbps:.0f} GB/s")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(out), flush=True)

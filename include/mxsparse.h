@@ -247,6 +247,20 @@ int decode_step_reuse(const mxs_step *step, const int32_t *block_table, void *ws
                       void *stream);
 
 /* ---- diagnostics ---------------------------------------------------------- */
+
+/* mxs_read_index_pages: a measurement aid, not a step of the method. It reads
+ * every index page of sequences 0..B-1 once (logical pages 0..ceil(L_b/128)-1
+ * through the page table, in page-table order, cache.idx_format's page size)
+ * with plain 16-byte loads and nothing else, so its time is the streaming-read
+ * ceiling of the scan that index_score performs (one workgroup per 4 logical
+ * pages of a sequence, 256 threads, every load requested before any is used).
+ * Page-table entries outside [0, num_pages) are not read.
+ *   sink   device, >= 4 bytes, 4-byte aligned: may receive one word, whose
+ *          value carries no meaning (it keeps the loads from being dropped)
+ * Errors: MXS_EINVAL / MXS_EUNSUPPORTED for the cache as index_score checks
+ * it (idx side only), B < 0 or a null / misaligned sink; MXS_ELAUNCH. */
+int mxs_read_index_pages(const mxs_cache *cache, int32_t B, uint32_t *sink, void *stream);
+
 const char *mxs_status_str(int status);
 const char *mxs_last_error(void);
 int mxs_abi_version(void);

@@ -25,7 +25,7 @@ EXPORTS = [
     "mxfp4_row_store", "fp8_row_store", "pack_q_e4m3", "index_score", "topk_blocks",
     "index_score_topk", "mxs_score_workspace_bytes", "sparse_split_attn", "mxs_default_partitions",
     "lse_merge", "decode_step", "decode_step_reuse", "mxs_workspace_bytes", "mxs_status_str", "mxs_last_error",
-    "mxs_abi_version",
+    "mxs_abi_version", "mxs_read_index_pages",
 ]
 
 
@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
             "lse_merge": [P, P, P, I32, I32, P, P, P],
             "decode_step": [P, P, SZ, P],
             "decode_step_reuse": [P, P, P, SZ, P],
+            "mxs_read_index_pages": [P, I32, P, P],
             "mxs_default_partitions": [I32, I32, I32],
             "mxs_score_workspace_bytes": [I32, I32, I32],
             "mxs_workspace_bytes": [I32, I32, I32, I32, I32, I32, I32],
@@ -199,6 +200,16 @@ def index_score(cache: Cache, q_idx, w, scores=None):
                              _dev(w, torch.float32, "w", (B, q, H_I)), B, q, H_I,
                              _dev(scores, torch.float32, "scores", (B, q, cache.stride)), _stream()))
     return scores
+
+
+def read_index_pages(cache: Cache, B, sink=None):
+    """Streaming read of every index page of sequences 0..B-1 (a measurement
+    aid: the scan's bandwidth ceiling; computes nothing of the method)."""
+    cache.check_batch(B)
+    if sink is None:
+        sink = torch.empty(1, dtype=torch.int32, device="cuda")
+    _check(lib().mxs_read_index_pages(cache.ref(), B, _dev(sink, torch.int32, "sink"), _stream()))
+    return sink
 
 
 def topk_blocks(cache: Cache, scores, topk, block_table=None):

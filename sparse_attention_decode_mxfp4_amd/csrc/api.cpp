@@ -289,6 +289,16 @@ int lse_merge(const float *sp_m, const float *sp_l, const float *sp_o, int32_t n
   return launched(mxs::launch_lse_merge(sp_m, sp_l, sp_o, n_rows, P, out, lse, (hipStream_t)stream), "lse_merge");
 }
 
+int mxs_read_index_pages(const mxs_cache *cache, int32_t B, uint32_t *sink, void *stream) {
+  if (int r = check_cache(cache, true, false)) return r;
+  REQ(B >= 0, MXS_EINVAL, "B: %d, must be >= 0", B);
+  REQ(sink && aligned(sink, 4), MXS_EINVAL, "sink: null or misaligned");
+  if (B == 0) return ok();
+  return launched(mxs::launch_read_pages(view(cache), B, (uint32_t)page_bytes(cache->idx_format), sink,
+                                         (hipStream_t)stream),
+                  "mxs_read_index_pages");
+}
+
 size_t mxs_workspace_bytes(int32_t B, int32_t q, int32_t H, int32_t H_I, int32_t topk, int32_t page_table_stride,
                            int32_t num_partitions) {
   (void)H_I;

@@ -69,6 +69,10 @@ hipError_t launch_table_attn(const CacheView &c, const int32_t *block_table, con
                              int32_t H, int32_t topk, int32_t P, float sm_scale, float *sp_m, float *sp_l, float *sp_o,
                              const FusedMerge &fm, hipStream_t s);
 
+// streaming read of every index page in page-table order (read.hip): a
+// measurement of the scan's bandwidth ceiling; sink receives at most one word
+hipError_t launch_read_pages(const CacheView &c, int32_t B, uint32_t page_bytes, uint32_t *sink, hipStream_t s);
+
 // merge (merge.hip)
 hipError_t launch_lse_merge(const float *sp_m, const float *sp_l, const float *sp_o, int32_t n_rows,
                             int32_t P, uint16_t *out, float *lse, hipStream_t s);

@@ -152,3 +152,14 @@ def test_decode_step_reuse_rejects_before_launch(L):
     s.q_dtype = mx.MXS_F32
     s.B = 0                           # an empty batch does nothing and succeeds
     assert L.decode_step_reuse(P(s), table, None, 0, None) == mx.MXS_OK
+
+
+def test_read_index_pages_rejects_before_launch(L):
+    P = ctypes.byref
+    sink = ctypes.c_void_p(256)
+    assert L.mxs_read_index_pages(P(_cache()), 1, None, None) == mx.MXS_EINVAL
+    assert L.mxs_read_index_pages(P(_cache()), 1, ctypes.c_void_p(258), None) == mx.MXS_EINVAL
+    assert L.mxs_read_index_pages(P(_cache()), -1, sink, None) == mx.MXS_EINVAL
+    assert L.mxs_read_index_pages(P(_cache(idx_pages=0)), 1, sink, None) == mx.MXS_EINVAL
+    assert L.mxs_read_index_pages(P(_cache(idx_format=2)), 1, sink, None) == mx.MXS_EUNSUPPORTED
+    assert L.mxs_read_index_pages(P(_cache()), 0, sink, None) == mx.MXS_OK    # nothing to read

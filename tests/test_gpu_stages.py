@@ -299,3 +299,25 @@ def test_lse_merge_partials(mx):
     assert (np.abs(Og - Oref) <= 2 ** -8 * np.abs(Oref) + 1e-5 * np.abs(Oref).max()).all()
     ok = np.isfinite(lref)
     np.testing.assert_allclose(lse.cpu().numpy()[ok], lref[ok], rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_read_index_pages_reads_and_writes_nothing_else(mx, name):
+    """The scan's read-ceiling launch (a measurement aid): it completes over
+    real tables and over tables holding entries outside the pool (skipped),
+    leaves the pages untouched and writes nothing but its one-word sink."""
+    inp, pools, cache, t = _setup(mx, name)
+    before = pools["idx"].clone()
+    guard = torch.zeros(64, dtype=torch.int32, device=DEV)      # sink = guard[0]; the rest must stay zero
+    mx.read_index_pages(cache, inp.wl.B, guard[:1])
+    table = cache.page_table.clone()
+    bad = cache.page_table.clone()
+    bad.view(-1)[::3] = -1
+    bad.view(-1)[1::3] = cache.num_pages + 7
+    cache.page_table.copy_(bad)
+    mx.read_index_pages(cache, inp.wl.B, guard[:1])
+    cache.page_table.copy_(table)
+    torch.cuda.synchronize()
+    assert torch.equal(pools["idx"], before)
+    assert int(guard[1:].abs().sum()) == 0
+    assert int(guard[0]) in (0, 0x9E3779B9 - (1 << 32))
