@@ -185,3 +185,26 @@ def test_reuse_step_alternating_tables_share_a_workspace(mx):
             assert torch.equal(s_.out, first[k][0]) and torch.equal(s_.lse, first[k][1]), f"run {i}, step {k}"
     r = OS.decode_step_reuse_ref(inp, random_table(inp, 1), seqs=[0])
     PT.check_attention(first[0][0].float().cpu().numpy()[0], r["O"][0], "alternating reuse b=0")
+
+
+def test_reuse_step_workspace_needs_no_initialization(mx):
+    """As for the full step: a workspace filled with 0xFF or 0x01 bytes gives
+    the output and lse of a zero-filled one, bit for bit."""
+    import workloads.gpu as WG
+    inp = W.make_inputs(W.WORKLOADS["mxfp4_65k"])
+    wl = inp.wl
+    pools = WG.fill_prefix(inp, WG.empty_pools(inp))
+    cache = WG.make_cache(inp, pools)
+    t = WG.step_tensors(inp)
+    nb = mx.workspace_bytes(wl.B, wl.q, wl.H, 1, wl.topk, cache.stride)
+    assert mx.lib().mxs_default_partitions(wl.B, wl.q, wl.topk) > 1
+    tb = torch.from_numpy(random_table(inp, 1).astype(np.int32)).cuda()
+    res = []
+    for fill in (0x00, 0xFF, 0x01):
+        ws = torch.full((nb,), fill, dtype=torch.uint8, device="cuda")
+        s_ = mx.DecodeStepReuse(cache, t["query"], tb, wl.sm_scale, k_new=t.get("k_new"), v_new=t.get("v_new"), ws=ws)
+        s_.run()
+        torch.cuda.synchronize()
+        res.append((s_.out.clone(), s_.lse.clone()))
+    for k in (1, 2):
+        assert torch.equal(res[k][0], res[0][0]) and torch.equal(res[k][1], res[0][1]), f"fill {k}"

@@ -200,3 +200,28 @@ def test_decode_step_alternating_inputs_share_a_workspace(mx, name):
     O = first[0][0].float().cpu().numpy()
     for b in (0, 1):
         PT.check_attention(O[b], r["O"][b], f"{name} b={b}")
+
+
+@pytest.mark.parametrize("name", ["mxfp4_65k", "fp8"])
+def test_decode_step_workspace_needs_no_initialization(mx, name):
+    """The workspace's contents before a call do not matter (the step clears
+    its merge counters itself): a workspace filled with 0xFF or 0x01 bytes
+    gives the output and lse of a zero-filled one, bit for bit."""
+    import workloads.gpu as WG
+    inp = W.make_inputs(W.WORKLOADS[name].with_(B=4))
+    wl = inp.wl
+    pools = WG.fill_prefix(inp, WG.empty_pools(inp))
+    cache = WG.make_cache(inp, pools)
+    t = WG.step_tensors(inp)
+    nb = mx.workspace_bytes(wl.B, wl.q, wl.H, wl.H_I, wl.topk, cache.stride)
+    assert mx.lib().mxs_default_partitions(wl.B, wl.q, wl.topk) > 1      # the merge counters are in use
+    res = []
+    for fill in (0x00, 0xFF, 0x01):
+        ws = torch.full((nb,), fill, dtype=torch.uint8, device="cuda")
+        s_ = mx.DecodeStep(cache, t["query"], t["q_idx"], t["w"], wl.topk, wl.sm_scale, k_new=t.get("k_new"),
+                           v_new=t.get("v_new"), idx_new=t.get("idx_new"), ws=ws)
+        s_.run()
+        torch.cuda.synchronize()
+        res.append((s_.out.clone(), s_.lse.clone()))
+    for k in (1, 2):
+        assert torch.equal(res[k][0], res[0][0]) and torch.equal(res[k][1], res[0][1]), f"fill {k}"
