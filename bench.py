@@ -223,6 +223,19 @@ def main():
     ms_step = wall * 1e3 / args.steps
     ev_ms_step = ev0.elapsed_time(ev1) / args.steps
 
+    # per-replay distribution (outside the timed region): each replay of the
+    # R-step graph bracketed by its own events; median and spread per step
+    rep_us = []
+    if chunk is not None:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(max(100, args.steps // R))]
+        for a_, b_ in evs:
+            a_.record()
+            chunk.replay()
+            b_.record()
+        torch.cuda.synchronize()
+        rep_us = sorted(a_.elapsed_time(b_) * 1e3 / R for a_, b_ in evs)
+
     # warm (MALL-resident) number: one replica, one graph of R steps on it
     warm = torch.cuda.CUDAGraph()
     with torch.cuda.graph(warm):
@@ -332,6 +345,9 @@ def main():
                 "frac": step_gbps / HBM_PEAK_GBPS, "index_bytes": ab["index_pages"],
                 "kv_bytes": ab["kv_pages"], "other_bytes": ab["other"]},
         "event_ms_per_step": ev_ms_step,
+        "replays": ({"n": len(rep_us), "steps_per_replay": R, "median_us_per_step": rep_us[len(rep_us) // 2],
+                     "p10_us_per_step": rep_us[len(rep_us) // 10], "p90_us_per_step": rep_us[(9 * len(rep_us)) // 10]}
+                    if rep_us else None),
         "warm_mall_ms_per_step": warm_ms,
         "roofline": {"bound": "hbm", "kernel": "index scorer (k_index_score)", "achieved": score_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": score_gbps / HBM_PEAK_GBPS,
@@ -351,6 +367,9 @@ def main():
                      "frac": reuse_gbps / HBM_PEAK_GBPS, "algorithmic_bytes_per_step": reuse_bytes},
     }
     log(f"[bench] attention-only step {reuse_us:.1f} us = {reuse_gbps:.0f} GB/s")
+    if rep_us:
+        log(f"[bench] per replay of {R} steps: median {rep_us[len(rep_us) // 2]:.1f} us per step "
+            f"(p10 {rep_us[len(rep_us) // 10]:.1f}, p90 {rep_us[(9 * len(rep_us)) // 10]:.1f}; {len(rep_us)} replays)")
     log(f"[bench] step {ms_step * 1e3:.1f} us (events {ev_ms_step * 1e3:.1f} us, warm {warm_ms * 1e3:.1f} us), "
         f"{step_gbps:.0f} GB/s; scorer {score_us:.1f} us = {score_gbps:.0f} GB/s; "
         f"read ceiling {read_us:.1f} us = {read_gbps:.0f} GB/s")
