@@ -5,9 +5,9 @@ commit messages of the MXFP4 index-cache commit and of the MXFP4 main-KV commit)
 a page holds 128 tokens of head_dim 128 as 4-bit e2m1 elements in 32-element
 groups, each group with one e8m0 (power-of-two) scale, 8704 bytes in all, and
 one layout serves the index keys, K and V. The pages name the quantizer
-(``mxfp4ScaleE8m0``) without defining it; the benchmark spec asks for an OCP-MX
-quantizer, so the scale is the OCP MX v1.0 rule: 2^(floor(log2 amax) - 2),
-where 2 is e2m1's largest exponent.
+(``mxfp4ScaleE8m0``) without defining it; the reading taken here is the OCP
+MX v1.0 quantizer, whose scale is 2^(floor(log2 amax) - 2), where 2 is e2m1's
+largest exponent.
 
 FP8 (ATOM PR #2686, "Enable Mono decode with fixed DSpark verify", Summary:
 "FP8 KV/index cache, block 128"; vLLM PR #60528, Details): e4m3 elements with

@@ -1,5 +1,5 @@
 """Parity helpers shared by the GPU tests: tolerances and comparisons against
-the oracle. Tolerances (derived in the design doc):
+the oracle. Tolerances, each with its derivation:
 
 - page bytes, q codes, block ids: exact;
 - block scores: |S_gpu - S_ref| <= 1e-5 * S_abs + 1e-30, where S_abs is the
