@@ -5,8 +5,9 @@
 One step = the whole hot path of one decode step over one batch: row store of
 the step's new K / V / index rows, e4m3 query store, index scores over every
 page, top-k, split attention over the selected pages and the merge
-(decode_step of libmxsparse; R consecutive steps, one per cache replica, are
-captured in one HIP graph, as the layers of a decode are). The default workload is
+(decode_step of libmxsparse). The K timed steps run on R cache replicas in
+turn (step i on replica i % R, as the layers of a decode each have their own
+cache) and are captured in one HIP graph of K steps, replayed once. The default workload is
 the 256K-context one: B = 4 sequences x q = 8 query rows (1 + 7 drafts), 16
 query heads per KV head, head_dim 128, MXFP4 K / V / index caches, top-k 32.
 
@@ -183,40 +184,39 @@ def main():
     torch.cuda.synchronize()
     ab = algorithmic_bytes(inp, tables[0].cpu().numpy())
 
-    # ---- the timed region: exactly K steps, rotating replicas. One HIP graph
-    # holds R consecutive steps (one per replica, like the layers of one decode
-    # step, each with its own cache); K = n * R + r runs n replays of it and r
-    # single-step graphs.
-    if args.eager:
-        chunk, single = None, [s.run for s in steps]
-    else:
-        chunk = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(chunk):
-            for s in steps:
-                s.run()
-        single = []
-        for s in steps:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                s.run()
-            single.append(g.replay)
-
-    def run_steps(k):
-        if chunk is None:
+    # ---- the timed region: exactly K steps, rotating replicas (step i runs on
+    # replica i % R, like the layers of one decode step, each with its own
+    # cache), captured in one HIP graph of K steps and replayed once, so no
+    # host launch gap falls between steps; the W warmup steps are a graph of
+    # their own.
+    def steps_graph(k):
+        if k <= 0:
+            return None
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
             for i in range(k):
-                single[i % R]()
-            return
-        for _ in range(k // R):
-            chunk.replay()
-        for i in range(k % R):
-            single[i]()
+                steps[i % R].run()
+        return g
 
-    run_steps(args.warmup)
+    if args.eager:
+        def run_steps(k):
+            for i in range(k):
+                steps[i % R].run()
+        warm_run = lambda: run_steps(args.warmup)
+        timed_run = lambda: run_steps(args.steps)
+    else:
+        g_warm, g_timed = steps_graph(args.warmup), steps_graph(args.steps)
+        warm_run = g_warm.replay if g_warm is not None else (lambda: None)
+        timed_run = g_timed.replay
+    # the same R-step graph used below for the per-replay distribution
+    chunk = None if args.eager else steps_graph(R)
+
+    warm_run()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
-    run_steps(args.steps)
+    timed_run()
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

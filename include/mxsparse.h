@@ -32,9 +32,10 @@
  *     next synchronization.
  *   - MXS_ELAUNCH reports a launch failure (hipGetLastError after enqueue).
  *
- * Cache page layouts (a reading of "a 16 B key load and a dword of e8m0 scales
- * a tile", same PR, commit message of the MXFP4 index-cache commit; one layout
- * serves the index keys, K and V, commit message of the MXFP4 main-KV commit):
+ * Cache page layouts (a reading: the scorer of the same PR reads a tile with one
+ * 16-byte load of key codes and one dword of e8m0 scales, commit message of the
+ * MXFP4 index-cache commit; one layout serves the index keys, K and V, commit
+ * message of the MXFP4 main-KV commit):
  *   MXFP4 page, 8704 B: token t (0..127) has its 128 e2m1 codes at bytes
  *     [64 t, 64 t + 64) — element 2i in the low nibble of byte i, 2i+1 in the
  *     high nibble — and its four e8m0 group scales (elements 0-31, 32-63, 64-95,

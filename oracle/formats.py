@@ -10,7 +10,7 @@ MX v1.0 quantizer, whose scale is 2^(floor(log2 amax) - 2), where 2 is e2m1's
 largest exponent.
 
 FP8 (ATOM PR #2686, "Enable Mono decode with fixed DSpark verify", Summary:
-"FP8 KV/index cache, block 128"; vLLM PR #60528, Details): e4m3 elements with
+an FP8 K/V and index cache in 128-token blocks; vLLM PR #60528, Details): e4m3 elements with
 a per-token fp32 scale. Reading (parity unpinned, the pages give no rule):
 scale = fp32(amax / 448), 1.0 for an all-zero row, code = e4m3(fp32(x / scale)).
 
@@ -18,8 +18,9 @@ e4m3 q store (ATOM PR #2812, commit message of the e4m3 q store, and the one
 that factors out ``pack_q_e4m3``): unit scale, round to nearest even, values
 beyond +-448 and +-inf saturate to +-448, NaN stays NaN.
 
-Page layouts (a reading; the pages say only "a 16 B key load and a dword of
-e8m0 scales" per tile, which this layout serves). Parity unpinned against the
+Page layouts (a reading; the pages only say that the scorer reads a tile with
+one 16-byte load of key codes plus one dword holding its e8m0 scales, which
+this layout allows). Parity unpinned against the
 pages' own writer, which is not available; oracle and library agree on it.
 
   MXFP4 page (8704 B): token t's 128 codes at [64 t, 64 t + 64), element 2i in

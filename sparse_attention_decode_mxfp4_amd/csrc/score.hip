@@ -17,11 +17,12 @@
 // Lane layout (lane = 16 kg + n): for an N-tile of 16 tokens the lane takes
 // the 16 bytes of token n's group kg — one 32-element group and its one scale
 // byte — so a wave's load instruction covers 16 whole token rows (1 KiB,
-// coalesced), copied straight into LDS (see dma_page). The MFMA's K index is permuted to match: k-step s, lane group
-// kg carries elements 32 kg + 8 s .. 32 kg + 8 s + 7, and the q_idx fragment
-// follows the same permutation ("q_frag follows the 32-element groups" in the
-// commit message). The result tile gives each lane the 4 index heads of one
-// query row for one token, so the head sum, ReLU, weights and causal mask stay
+// coalesced), copied straight into LDS (see dma_page). The MFMA's K index is
+// permuted to match: k-step s, lane group kg carries elements 32 kg + 8 s ..
+// 32 kg + 8 s + 7, and the q_idx fragment follows the same permutation (the
+// commit message lays the query fragment out along the 32-element groups as
+// well). The result tile gives each lane the 4 index heads of one query row
+// for one token, so the head sum, ReLU, weights and causal mask stay
 // in the lane, and the block max is a 16-lane reduction per page.
 #include "common.hpp"
 #include "launch.hpp"

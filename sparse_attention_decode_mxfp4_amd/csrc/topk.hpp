@@ -3,7 +3,7 @@
 //
 // ATOM PR #2686 ("Enable Mono decode with fixed DSpark verify", the review
 // thread's commit message: each sparse layer selects its own sparse blocks)
-// and PR #2812 (a selected block is one page-128 page in the sparse table).
+// and PR #2812 (each block the selection names is one 128-token page).
 // The k highest scores win; equal scores go to the lower block id; a row with
 // no more than k candidates keeps all of them; ids come out ascending.
 //

@@ -127,19 +127,87 @@ def test_decode_step_empty_batch(mx):
     assert step.out.numel() == 0
 
 
-@pytest.mark.parametrize("name,seqs", [("long", [0, 2]), ("headline", [1]), ("b32", [0, 17, 31])])
-def test_decode_step_full_size_sampled(mx, name, seqs):
-    inp = W.make_inputs(W.WORKLOADS[name])
+# One GPU run per full-size workload (and partition count), kept while its
+# sequences are checked one test at a time; the oracle recomputes each
+# sequence on its own.
+_RUNS = {}
+
+
+def cached_run(mx, name, P=0, **kw):
+    key = (name, P, tuple(sorted(kw.items())))
+    if key not in _RUNS:
+        _RUNS.clear()
+        wl = W.WORKLOADS[name].with_(**kw) if kw else W.WORKLOADS[name]
+        inp = W.make_inputs(wl)
+        _RUNS[key] = (inp, run_step(mx, inp, num_partitions=P))
+    return _RUNS[key]
+
+
+B32_SEQS = (0, 4, 9, 13, 17, 22, 26, 31)
+
+
+@pytest.mark.parametrize("name,b", [("headline", b) for b in range(4)] + [("long", b) for b in range(4)]
+                         + [("b32", b) for b in B32_SEQS])
+def test_decode_step_full_size(mx, name, b):
+    """The bench's workloads in the launch configuration it times: every
+    sequence of the 256K and ragged 128K-256K steps, 8 of the 32 sequences of
+    the B = 32 step, each against the oracle's step for that sequence."""
+    inp, g = cached_run(mx, name)
+    check_step(inp, g, [b])
+    if b == 0:
+        # every row of every sequence: finite output and a valid selection
+        # (min(k, candidates) ascending ids below the row's candidate count)
+        assert np.isfinite(g["O"]).all()
+        for bb in range(inp.wl.B):
+            nc = OI.n_candidates(int(inp.contexts[bb]), inp.wl.q)
+            for j in range(inp.wl.q):
+                sel = g["table"][bb, j]
+                k = min(inp.wl.topk, int(nc[j]))
+                assert (sel[:k] >= 0).all() and (np.diff(sel[:k]) > 0).all() and sel[k - 1] < nc[j]
+                assert (sel[k:] == -1).all()
+
+
+@pytest.mark.parametrize("b", [0, 3])
+def test_decode_step_long_with_empty_partitions(mx, b):
+    """The ragged 128K-256K workload with 24 partitions for top-k 32: each
+    partition holds ceil(32 / 24) = 2 slots, so partitions 16..23 of every
+    row are empty and merge in as (-inf, 0, 0)."""
+    inp, g = cached_run(mx, "long", P=24)
+    check_step(inp, g, [b])
+
+
+@pytest.mark.parametrize("kw", [
+    # 4-wave x 1-page scorer workgroups (4 pages each): the 8 new rows at 508..515 and
+    # 1020..1027 fall on both sides of a workgroup boundary (pages 3 | 4 and 7 | 8)
+    dict(B=2, ctx_rule=("list", (516, 1028)), topk=16),
+    # 4 x 4 pages (16-page workgroups; 4096 pages in all): boundaries at 2048-token multiples
+    dict(B=4, ctx_rule=("list", (131072, 2052, 4100, 8196)), topk=16),
+    # 4 x 8 pages (32-page workgroups; 8192 pages in all): boundaries at 4096-token multiples
+    dict(B=4, ctx_rule=("list", (262144, 4100, 8196, 65540)), topk=32),
+])
+def test_decode_step_new_rows_straddle_scorer_workgroups(mx, kw):
+    """The step's new index rows split between two scorer workgroups, in each
+    of the scorer's launch shapes for MXFP4 pages."""
+    wl = W.WORKLOADS["mxfp4_65k"].with_(name="straddle", **kw)
+    inp = W.make_inputs(wl)
     g = run_step(mx, inp)
-    check_step(inp, g, seqs)
-    # every row of every sequence: finite output, a valid selection
-    assert np.isfinite(g["O"]).all()
-    for b in range(inp.wl.B):
-        nc = OI.n_candidates(int(inp.contexts[b]), inp.wl.q)
-        for j in range(inp.wl.q):
-            sel = g["table"][b, j]
-            k = min(inp.wl.topk, int(nc[j]))
-            assert (sel[:k] >= 0).all() and (np.diff(sel[:k]) > 0).all() and sel[k - 1] < nc[j]
+    check_step(inp, g, range(wl.B))
+
+
+def test_decode_step_wide_page_table(mx):
+    """The 65K workload with its page table padded to 4096 entries per
+    sequence (-1 past each sequence): the scorer's 32-page workgroups past the
+    context and the selection's 32-candidates-per-thread variant."""
+    inp, g = cached_run(mx, "mxfp4_65k", table_stride=4096)
+    assert inp.max_pages == 4096
+    check_step(inp, g, range(inp.wl.B))
+
+
+def test_decode_step_fp8_65k(mx):
+    """The FP8 workload at 65536 tokens (2048 pages in all): the scorer's
+    2-pages-per-wave shape for FP8 pages."""
+    inp, g = cached_run(mx, "fp8", ctx_rule=("fixed", 65536))
+    check_step(inp, g, range(inp.wl.B))
 
 
 @pytest.mark.parametrize("name", ["mxfp4_65k", "fp8"])

@@ -232,6 +232,41 @@ def test_mxfp4_byte_layout():
     assert (pool[128:8192] == 0xFF).all() and (pool[8200:] == 0xFF).all()
 
 
+def test_fp8_byte_layout():
+    """Token t of an FP8 page: 128 e4m3 codes at 128 t, its fp32 scale (little
+    endian) at 16384 + 4 t; worked bytes from a row with a known amax."""
+    x = np.zeros((3, 128), dtype=np.float32)
+    x[2, 0] = 448.0 * 4.0         # amax 1792 -> scale 4.0 (0x40800000); 1792 / 4 = 448 -> code 0x7E
+    x[2, 5] = -1.0                # -1 / 4 = -0.25 = 2^-2 -> exponent field 5, mantissa 0 -> 0xA8
+    x[2, 127] = 2.0               # 0.5 = 2^-1 -> exponent field 6 -> 0x30
+    pool = W.new_pool(1, F.FP8_PAGE_BYTES)
+    F.fp8_store(pool, np.array([0], dtype=np.int32), 1, x[1:])     # positions 1 and 2
+    row2 = pool[256:384]
+    assert row2[0] == 0x7E and row2[5] == 0xA8 and row2[127] == 0x30
+    assert (np.delete(row2, [0, 5, 127]) == 0).all()
+    assert (pool[128:256] == 0).all()                               # the all-zero row: codes 0
+    assert list(pool[16384 + 8:16384 + 12]) == [0x00, 0x00, 0x80, 0x40]    # 4.0f, little endian
+    assert list(pool[16384 + 4:16384 + 8]) == [0x00, 0x00, 0x80, 0x3F]     # 1.0f for the zero row
+    assert (pool[:128] == 0xFF).all() and (pool[384:16384] == 0xFF).all()  # other slots untouched
+    assert (pool[16384:16388] == 0xFF).all() and (pool[16396:] == 0xFF).all()
+    # and the read path takes the same bytes back: code * scale
+    got = F.fp8_read(pool, np.array([0], dtype=np.int32), 3, np.array([2]))
+    assert got[0, 0] == 1792.0 and got[0, 5] == -1.0 and got[0, 127] == 2.0
+
+
+def test_bf16_to_f64_matches_torch_all_patterns():
+    """Every one of the 65536 bf16 bit patterns decodes as torch's
+    bfloat16 -> float32 conversion does (NaNs compared as NaN)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float32).numpy()
+    with np.errstate(invalid="ignore"):          # NaN payloads widen with a warning, not an error
+        got = F.bf16_to_f64(bits)
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all()
+    np.testing.assert_array_equal(got[~nan], ref[~nan].astype(np.float64))
+    assert (np.signbit(got[~nan]) == np.signbit(ref[~nan])).all()       # -0 keeps its sign
+
+
 def test_page_table_permutation_invariance():
     """Relabelling physical pages (and moving their bytes) leaves every read bit-identical."""
     rng = np.random.default_rng(4)

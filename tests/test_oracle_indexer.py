@@ -106,6 +106,32 @@ def test_fewer_candidates_than_k():
     assert list(I.topk_blocks(s, 3, 5)) == [0, 1, 2, -1, -1]
 
 
+def test_kth_score_worked_values():
+    s = np.array([1.0, 5.0, 3.0, 5.0, 2.0, -np.inf])
+    assert I.kth_score(s, 5, 1) == 5.0
+    assert I.kth_score(s, 5, 2) == 5.0          # a tie at the top counts twice
+    assert I.kth_score(s, 5, 3) == 3.0
+    assert I.kth_score(s, 5, 5) == 1.0
+    assert I.kth_score(s, 5, 9) == 1.0          # fewer candidates than k: the smallest candidate
+    assert I.kth_score(s, 2, 4) == 1.0          # only the first n_cand entries are candidates
+    assert I.kth_score(s, 6, 6) == -np.inf
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.lists(st.integers(-3, 3), min_size=1, max_size=40), st.integers(1, 50), st.integers(0, 40))
+def test_kth_score_brute_force(vals, k, cut):
+    """The k-th largest candidate score equals the score of the k-th member of
+    the brute-force ordering by (score desc, id asc), and is the score of the
+    lowest-ranked block top-k keeps."""
+    s = np.array(vals, dtype=np.float64)
+    n = max(1, min(len(vals), cut or len(vals)))
+    ranked = sorted(range(n), key=lambda i: (-s[i], i))
+    kk = min(k, n)
+    assert I.kth_score(s, n, k) == s[ranked[kk - 1]]
+    kept = [i for i in I.topk_blocks(s, n, k) if i >= 0]
+    assert I.kth_score(s, n, k) == min(s[i] for i in kept)
+
+
 @settings(max_examples=300, deadline=None)
 @given(st.lists(st.integers(-3, 3), min_size=1, max_size=40), st.integers(1, 12))
 def test_topk_characterisation(vals, k):

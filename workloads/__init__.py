@@ -62,6 +62,7 @@ class Workload:
     ctx_rule: tuple        # ("fixed", L) | ("fixed_minus_u", L, umax) | ("uniform", lo, hi) | ("list", (...))
     full_step: bool = True # the step's q new rows are stored by the step itself
     pool_slack: float = 1.25
+    table_stride: int = 0  # page-table row length; 0 = the longest sequence's page count
 
     # ---- context lengths -------------------------------------------------
     def contexts(self) -> np.ndarray:
@@ -186,7 +187,7 @@ def make_inputs(wl: Workload, inject_q: bool = False) -> StepInputs:
     n_pages = np.array([pages_for(L) for L in ctx], dtype=np.int64)
     need = int(n_pages.sum())
     num_pages = int(math.ceil(need * wl.pool_slack)) + 1
-    max_pages = int(n_pages.max())
+    max_pages = max(int(n_pages.max()), int(wl.table_stride))      # rows padded with -1 past a sequence
     rng = np.random.default_rng([wl.seed, _S_TABLE])
     perm = rng.permutation(num_pages)[:need].astype(np.int32)
     table = np.full((wl.B, max_pages), -1, dtype=np.int32)
