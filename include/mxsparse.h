@@ -247,6 +247,25 @@ size_t mxs_workspace_bytes(int32_t B, int32_t q, int32_t H, int32_t H_I, int32_t
 int decode_step_reuse(const mxs_step *step, const int32_t *block_table, void *ws, size_t ws_bytes,
                       void *stream);
 
+/* decode_step_noalloc: decode_step for callers that cannot allocate device
+ * memory (code under HIP graph capture that may not allocate, tight serving
+ * loops, harnesses that forbid allocation). Same arguments, results, errors
+ * and launches as decode_step, but the workspace is a device array the
+ * library holds: MXS_NOALLOC_SCRATCH_BYTES bytes on each GPU it runs on, kept
+ * until the process ends. Its device address is looked up once per device
+ * (the calling thread's current device, which `stream` must belong to).
+ * Nothing is allocated or freed by the call.
+ *   Errors: MXS_EWORKSPACE when the step needs more workspace than the array
+ *   holds (mxs_workspace_bytes(...) > MXS_NOALLOC_SCRATCH_BYTES: e.g. 4
+ *   sequences x 8 rows at 256K context need about 2.4 MB, 32 x 8 about 4.6 MB);
+ *   MXS_ELAUNCH when there is no usable current device; otherwise as
+ *   decode_step.
+ *   Concurrency: every call on one GPU shares that GPU's array (its contents
+ *   from an earlier call do not matter); calls that overlap on one GPU — two
+ *   streams, two threads — race on it and must be serialized by the caller. */
+#define MXS_NOALLOC_SCRATCH_BYTES (8u << 20)
+int decode_step_noalloc(const mxs_step *step, void *stream);
+
 /* ---- diagnostics ---------------------------------------------------------- */
 
 /* mxs_read_index_pages: a measurement aid, not a step of the method. It reads

@@ -25,8 +25,9 @@ EXPORTS = [
     "mxfp4_row_store", "fp8_row_store", "pack_q_e4m3", "index_score", "topk_blocks",
     "index_score_topk", "mxs_score_workspace_bytes", "sparse_split_attn", "mxs_default_partitions",
     "lse_merge", "decode_step", "decode_step_reuse", "mxs_workspace_bytes", "mxs_status_str", "mxs_last_error",
-    "mxs_abi_version", "mxs_read_index_pages",
+    "mxs_abi_version", "mxs_read_index_pages", "decode_step_noalloc",
 ]
+NOALLOC_SCRATCH_BYTES = 8 << 20        # MXS_NOALLOC_SCRATCH_BYTES
 
 
 class MxsError(RuntimeError):
@@ -80,6 +81,7 @@ def lib() -> ctypes.CDLL:
             "lse_merge": [P, P, P, I32, I32, P, P, P],
             "decode_step": [P, P, SZ, P],
             "decode_step_reuse": [P, P, P, SZ, P],
+            "decode_step_noalloc": [P, P],
             "mxs_read_index_pages": [P, I32, P, P],
             "mxs_default_partitions": [I32, I32, I32],
             "mxs_score_workspace_bytes": [I32, I32, I32],
@@ -294,10 +296,15 @@ def workspace_bytes(B, q, H, H_I, topk, stride, num_partitions=0) -> int:
 
 class DecodeStep:
     """decode_step over fixed tensors: builds the argument struct once, so that
-    ``run()`` is a single C call (the launch chain), fit for timing and capture."""
+    ``run()`` is a single C call (the launch chain), fit for timing and capture.
+
+    With ``noalloc=True`` no workspace is taken or allocated and ``run()``
+    calls decode_step_noalloc, whose workspace is the library's own device
+    array (out and lse are still allocated here unless given)."""
 
     def __init__(self, cache: Cache, query, q_idx, w, topk, sm_scale, k_new=None, v_new=None, idx_new=None,
-                 num_partitions=0, out=None, lse=None, block_table_out=None, scores_out=None, ws=None):
+                 num_partitions=0, out=None, lse=None, block_table_out=None, scores_out=None, ws=None,
+                 noalloc=False):
         B, q, H, _ = query.shape
         cache.check_batch(B)
         H_I = q_idx.shape[2]
@@ -311,7 +318,11 @@ class DecodeStep:
         self.out = out if out is not None else torch.empty((B, q, H, 128), dtype=torch.bfloat16, device=dev)
         self.lse = lse if lse is not None else torch.empty((B, q, H), dtype=torch.float32, device=dev)
         nb = workspace_bytes(B, q, H, H_I, topk, cache.stride, num_partitions)
-        self.ws = ws if ws is not None else torch.empty(nb, dtype=torch.uint8, device=dev)
+        self.noalloc = noalloc
+        if noalloc:
+            self.ws = None
+        else:
+            self.ws = ws if ws is not None else torch.empty(nb, dtype=torch.uint8, device=dev)
         self.cache = cache
         self._keep = (query, q_idx, w, k_new, v_new, idx_new, block_table_out, scores_out)
         self.block_table_out, self.scores_out = block_table_out, scores_out
@@ -325,13 +336,17 @@ class DecodeStep:
             _dev(self.out, torch.bfloat16, "out", (B, q, H, 128)), _opt(self.lse, torch.float32, "lse", (B, q, H)),
             _opt(block_table_out, torch.int32, "block_table_out", (B, q, topk)),
             _opt(scores_out, torch.float32, "scores_out", (B, q, cache.stride)))
-        if self.ws.numel() < nb:
-            raise ValueError(f"ws: {self.ws.numel()} bytes, needs {nb}")
-        self._ws_ptr = _dev(self.ws, torch.uint8, "ws")
+        if not noalloc:
+            if self.ws.numel() < nb:
+                raise ValueError(f"ws: {self.ws.numel()} bytes, needs {nb}")
+            self._ws_ptr = _dev(self.ws, torch.uint8, "ws")
 
     def run(self, stream=None):
         s = _stream() if stream is None else stream
-        _check(lib().decode_step(ctypes.byref(self.struct), self._ws_ptr, self.ws.numel(), s))
+        if self.noalloc:
+            _check(lib().decode_step_noalloc(ctypes.byref(self.struct), s))
+        else:
+            _check(lib().decode_step(ctypes.byref(self.struct), self._ws_ptr, self.ws.numel(), s))
         return self.out
 
 

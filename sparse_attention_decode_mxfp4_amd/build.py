@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmxsparse.so")
-SOURCES = ["api.cpp", "store.hip", "score.hip", "topk.hip", "attn.hip", "merge.hip", "read.hip"]
+SOURCES = ["api.cpp", "store.hip", "score.hip", "topk.hip", "attn.hip", "merge.hip", "read.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

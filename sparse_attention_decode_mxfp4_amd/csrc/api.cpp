@@ -29,6 +29,14 @@ int ok() {
   return MXS_OK;
 }
 
+}  // namespace
+
+namespace mxs {
+int api_error(int code, const char *msg) { return fail(code, "%s", msg); }
+}  // namespace mxs
+
+namespace {
+
 int launched(hipError_t e, const char *what) {
   if (e != hipSuccess) return fail(MXS_ELAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
   return ok();

@@ -73,6 +73,10 @@ hipError_t launch_table_attn(const CacheView &c, const int32_t *block_table, con
 // measurement of the scan's bandwidth ceiling; sink receives at most one word
 hipError_t launch_read_pages(const CacheView &c, int32_t B, uint32_t page_bytes, uint32_t *sink, hipStream_t s);
 
+// sets the thread-local message that mxs_last_error() returns and gives back
+// `code` (api.cpp; for entry points defined in other sources)
+int api_error(int code, const char *msg);
+
 // merge (merge.hip)
 hipError_t launch_lse_merge(const float *sp_m, const float *sp_l, const float *sp_o, int32_t n_rows,
                             int32_t P, uint16_t *out, float *lse, hipStream_t s);

@@ -31,7 +31,7 @@ def test_header_declares_the_stages():
               "index_score_topk", "sparse_split_attn", "lse_merge", "decode_step", "decode_step_reuse",
               "mxs_workspace_bytes",
               "mxs_default_partitions", "mxs_status_str", "mxs_last_error", "mxs_abi_version",
-              "mxs_score_workspace_bytes"]:
+              "mxs_score_workspace_bytes", "decode_step_noalloc"]:
         assert f in names, f
     assert set(names) == set(mx.EXPORTS)
 
@@ -163,3 +163,20 @@ def test_read_index_pages_rejects_before_launch(L):
     assert L.mxs_read_index_pages(P(_cache(idx_pages=0)), 1, sink, None) == mx.MXS_EINVAL
     assert L.mxs_read_index_pages(P(_cache(idx_format=2)), 1, sink, None) == mx.MXS_EUNSUPPORTED
     assert L.mxs_read_index_pages(P(_cache()), 0, sink, None) == mx.MXS_OK    # nothing to read
+
+
+def test_noalloc_refuses_steps_beyond_its_scratch(L):
+    """decode_step_noalloc refuses, before touching any device, a step whose
+    workspace would exceed the library's array (MXS_NOALLOC_SCRATCH_BYTES)."""
+    text = open(HEADER).read()
+    assert "#define MXS_NOALLOC_SCRATCH_BYTES (8u << 20)" in text
+    assert mx.NOALLOC_SCRATCH_BYTES == 8 << 20
+    assert L.decode_step_noalloc(None, None) == mx.MXS_EINVAL
+    # 64 sequences x 8 rows over 8192-page tables: 16 MiB of scores alone
+    st = mx.StepStruct()
+    st.cache.page_table_stride = 8192
+    st.B, st.q, st.H, st.H_I, st.topk = 64, 8, 16, 4, 32
+    need = L.mxs_workspace_bytes(64, 8, 16, 4, 32, 8192, 0)
+    assert need > mx.NOALLOC_SCRATCH_BYTES
+    assert L.decode_step_noalloc(ctypes.byref(st), None) == mx.MXS_EWORKSPACE
+    assert "scratch" in _err(L) and str(need) in _err(L)
