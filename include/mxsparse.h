@@ -228,6 +228,35 @@ int decode_step(const mxs_step *step, void *ws, size_t ws_bytes, void *stream);
 size_t mxs_workspace_bytes(int32_t B, int32_t q, int32_t H, int32_t H_I, int32_t topk,
                            int32_t page_table_stride, int32_t num_partitions);
 
+/* decode_step_one_launch: the same step, results bit for bit those of
+ * decode_step, as ONE launch (the single-launch step of the pages' persistent
+ * decode kernel, vLLM PR #60528, Merge Danger, which assumes every workgroup
+ * co-resident). The grid holds the scoring workgroups first, then the
+ * attention workgroups. A scoring workgroup writes its scores, its share of
+ * the step's K / V rows and of the e4m3 query with device-coherent stores and
+ * counts itself in for its sequence; an attention workgroup waits for its
+ * sequence's count, then selects, attends and merges. An attention workgroup
+ * only waits for workgroups with lower ids, which in-order dispatch has
+ * already started and which wait for nothing, so no co-residency is assumed;
+ * the wait is also bounded (about a second), so a launch always ends.
+ *   Supported: MXFP4 K / V and index caches, q <= 8 query rows and
+ *   B x page_table_stride >= 8192 pages (else MXS_EUNSUPPORTED, nothing
+ *   launched).
+ *   ws: as for decode_step, but zero-filled before its first use
+ *   (mxs_workspace_init, or a zero-filled allocation): it also holds
+ *   per-sequence counters, and every call leaves them zero again, so one
+ *   workspace serves any number of calls in stream order.
+ *   Measured on MI355X (4 x 8 rows, 256K context): slower than decode_step
+ *   (44 us against 36 us per step): its attention workgroups need the whole
+ *   register file of a CU, so none can start until a scoring workgroup has
+ *   left its CU, and the scan inside the larger kernel runs slower (22.7 us
+ *   against 19.2 us alone). */
+int decode_step_one_launch(const mxs_step *step, void *ws, size_t ws_bytes, void *stream);
+/* mxs_workspace_init: zero-fill ws_bytes (a multiple of 4) of a workspace on
+ * `stream` (a kernel, not a memset, so it may be captured in a HIP graph).
+ * Errors: MXS_EINVAL for a null or misaligned ws; MXS_ELAUNCH. */
+int mxs_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
 /* decode_step_reuse: the step of a layer that reuses an earlier layer's sparse
  * block selection instead of making its own (ATOM PR #2686, "Enable Mono
  * decode with fixed DSpark verify": under an index_topk_freq schedule some
@@ -252,8 +281,9 @@ int decode_step_reuse(const mxs_step *step, const int32_t *block_table, void *ws
  * loops, harnesses that forbid allocation). Same arguments, results, errors
  * and launches as decode_step, but the workspace is a device array the
  * library holds: MXS_NOALLOC_SCRATCH_BYTES bytes on each GPU it runs on, kept
- * until the process ends. Its device address is looked up once per device
- * (the calling thread's current device, which `stream` must belong to).
+ * until the process ends, zero when the library is loaded (every call leaves
+ * its counter words zero again). Its device address is looked up once per
+ * device (the calling thread's current device, which `stream` must belong to).
  * Nothing is allocated or freed by the call.
  *   Errors: MXS_EWORKSPACE when the step needs more workspace than the array
  *   holds (mxs_workspace_bytes(...) > MXS_NOALLOC_SCRATCH_BYTES: e.g. 4
@@ -261,8 +291,9 @@ int decode_step_reuse(const mxs_step *step, const int32_t *block_table, void *ws
  *   MXS_ELAUNCH when there is no usable current device; otherwise as
  *   decode_step.
  *   Concurrency: every call on one GPU shares that GPU's array (its contents
- *   from an earlier call do not matter); calls that overlap on one GPU — two
- *   streams, two threads — race on it and must be serialized by the caller. */
+ *   from an earlier call, counters back at zero, do not matter); calls that
+ *   overlap on one GPU — two streams, two threads — race on it and must be
+ *   serialized by the caller. */
 #define MXS_NOALLOC_SCRATCH_BYTES (8u << 20)
 int decode_step_noalloc(const mxs_step *step, void *stream);
 

@@ -25,7 +25,8 @@ EXPORTS = [
     "mxfp4_row_store", "fp8_row_store", "pack_q_e4m3", "index_score", "topk_blocks",
     "index_score_topk", "mxs_score_workspace_bytes", "sparse_split_attn", "mxs_default_partitions",
     "lse_merge", "decode_step", "decode_step_reuse", "mxs_workspace_bytes", "mxs_status_str", "mxs_last_error",
-    "mxs_abi_version", "mxs_read_index_pages", "decode_step_noalloc",
+    "mxs_abi_version", "mxs_read_index_pages", "decode_step_noalloc", "mxs_workspace_init",
+    "decode_step_one_launch",
 ]
 NOALLOC_SCRATCH_BYTES = 8 << 20        # MXS_NOALLOC_SCRATCH_BYTES
 
@@ -82,6 +83,8 @@ def lib() -> ctypes.CDLL:
             "decode_step": [P, P, SZ, P],
             "decode_step_reuse": [P, P, P, SZ, P],
             "decode_step_noalloc": [P, P],
+            "mxs_workspace_init": [P, SZ, P],
+            "decode_step_one_launch": [P, P, SZ, P],
             "mxs_read_index_pages": [P, I32, P, P],
             "mxs_default_partitions": [I32, I32, I32],
             "mxs_score_workspace_bytes": [I32, I32, I32],
@@ -294,17 +297,25 @@ def workspace_bytes(B, q, H, H_I, topk, stride, num_partitions=0) -> int:
     return lib().mxs_workspace_bytes(B, q, H, H_I, topk, stride, num_partitions)
 
 
+def workspace_init(ws):
+    """Zero-fill a step workspace (uint8 GPU tensor, 256-byte aligned) on the current stream."""
+    _check(lib().mxs_workspace_init(_dev(ws, torch.uint8, "ws"), ws.numel(), _stream()))
+    return ws
+
+
 class DecodeStep:
     """decode_step over fixed tensors: builds the argument struct once, so that
     ``run()`` is a single C call (the launch chain), fit for timing and capture.
 
     With ``noalloc=True`` no workspace is taken or allocated and ``run()``
     calls decode_step_noalloc, whose workspace is the library's own device
-    array (out and lse are still allocated here unless given)."""
+    array (out and lse are still allocated here unless given). With
+    ``one_launch=True`` ``run()`` calls decode_step_one_launch (the workspace
+    allocated here starts zero-filled, as that entry point requires)."""
 
     def __init__(self, cache: Cache, query, q_idx, w, topk, sm_scale, k_new=None, v_new=None, idx_new=None,
                  num_partitions=0, out=None, lse=None, block_table_out=None, scores_out=None, ws=None,
-                 noalloc=False):
+                 noalloc=False, one_launch=False):
         B, q, H, _ = query.shape
         cache.check_batch(B)
         H_I = q_idx.shape[2]
@@ -318,11 +329,11 @@ class DecodeStep:
         self.out = out if out is not None else torch.empty((B, q, H, 128), dtype=torch.bfloat16, device=dev)
         self.lse = lse if lse is not None else torch.empty((B, q, H), dtype=torch.float32, device=dev)
         nb = workspace_bytes(B, q, H, H_I, topk, cache.stride, num_partitions)
-        self.noalloc = noalloc
+        self.noalloc, self.one_launch = noalloc, one_launch
         if noalloc:
             self.ws = None
         else:
-            self.ws = ws if ws is not None else torch.empty(nb, dtype=torch.uint8, device=dev)
+            self.ws = ws if ws is not None else torch.zeros(nb, dtype=torch.uint8, device=dev)
         self.cache = cache
         self._keep = (query, q_idx, w, k_new, v_new, idx_new, block_table_out, scores_out)
         self.block_table_out, self.scores_out = block_table_out, scores_out
@@ -345,6 +356,8 @@ class DecodeStep:
         s = _stream() if stream is None else stream
         if self.noalloc:
             _check(lib().decode_step_noalloc(ctypes.byref(self.struct), s))
+        elif self.one_launch:
+            _check(lib().decode_step_one_launch(ctypes.byref(self.struct), self._ws_ptr, self.ws.numel(), s))
         else:
             _check(lib().decode_step(ctypes.byref(self.struct), self._ws_ptr, self.ws.numel(), s))
         return self.out
@@ -371,7 +384,7 @@ class DecodeStepReuse:
         self.out = out if out is not None else torch.empty((B, q, H, 128), dtype=torch.bfloat16, device=dev)
         self.lse = lse if lse is not None else torch.empty((B, q, H), dtype=torch.float32, device=dev)
         nb = workspace_bytes(B, q, H, 1, topk, cache.stride, num_partitions)
-        self.ws = ws if ws is not None else torch.empty(nb, dtype=torch.uint8, device=dev)
+        self.ws = ws if ws is not None else torch.zeros(nb, dtype=torch.uint8, device=dev)
         if self.ws.numel() < nb:
             raise ValueError(f"ws: {self.ws.numel()} bytes, needs {nb}")
         self.cache = cache

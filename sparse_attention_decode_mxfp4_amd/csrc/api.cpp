@@ -115,7 +115,7 @@ int default_partitions(int32_t B, int32_t q_rows, int32_t topk) {
 
 // workspace segments of decode_step, in order
 struct StepWs {
-  size_t scores, table, q8, sp_m, sp_l, sp_o, counters, total;
+  size_t scores, table, q8, sp_m, sp_l, sp_o, counters, seq_cnt, total;
 };
 
 StepWs step_ws(int32_t B, int32_t q, int32_t H, int32_t topk, int32_t stride, int32_t P) {
@@ -129,6 +129,7 @@ StepWs step_ws(int32_t B, int32_t q, int32_t H, int32_t topk, int32_t stride, in
   w.sp_l = off;   off += round_up(rows * H * P * sizeof(float));
   w.sp_o = off;   off += round_up(rows * H * P * MXS_HEAD_DIM * sizeof(float));
   w.counters = off; off += round_up(rows * sizeof(uint32_t));
+  w.seq_cnt = off;  off += round_up((size_t)B * 2 * sizeof(uint32_t));
   w.total = off;
   return w;
 }
@@ -315,7 +316,18 @@ size_t mxs_workspace_bytes(int32_t B, int32_t q, int32_t H, int32_t H_I, int32_t
   return step_ws(B, q, H, topk, page_table_stride, P).total;
 }
 
-int decode_step(const mxs_step *a, void *ws, size_t ws_bytes, void *stream) {
+int mxs_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+  REQ(ws || ws_bytes == 0, MXS_EINVAL, "mxs_workspace_init: ws null");
+  REQ(aligned(ws, 256), MXS_EINVAL, "mxs_workspace_init: ws not 256-byte aligned");
+  REQ(ws_bytes % 4 == 0, MXS_EINVAL, "mxs_workspace_init: ws_bytes %zu not a multiple of 4", ws_bytes);
+  if (ws_bytes == 0) return ok();
+  return launched(mxs::launch_zero(static_cast<uint32_t *>(ws), ws_bytes / 4, (hipStream_t)stream),
+                  "mxs_workspace_init");
+}
+
+// The argument checks of decode_step (and of decode_step_one_launch), then
+// the launches of the one or the other.
+static int step_entry(const mxs_step *a, void *ws, size_t ws_bytes, void *stream, bool one_launch) {
   REQ(a, MXS_EINVAL, "step: null");
   const mxs_cache *cache = &a->cache;
   if (int r = check_cache(cache, true, true)) return r;
@@ -357,8 +369,37 @@ int decode_step(const mxs_step *a, void *ws, size_t ws_bytes, void *stream) {
   float *sp_l = reinterpret_cast<float *>(base + w.sp_l);
   float *sp_o = reinterpret_cast<float *>(base + w.sp_o);
   uint32_t *counters = reinterpret_cast<uint32_t *>(base + w.counters);
+  uint32_t *seq_cnt = reinterpret_cast<uint32_t *>(base + w.seq_cnt);
   const hipStream_t s = (hipStream_t)stream;
   const mxs::CacheView c = view(cache);
+  const void *qa = mx ? static_cast<const void *>(q8) : a->query;
+  mxs::FusedMerge fm;
+  fm.counters = counters;
+  fm.out = a->out;
+  fm.lse = a->lse;
+
+  if (one_launch) {
+    // the whole step as one launch: scoring workgroups (with the row and query
+    // stores, device-coherent), then attention workgroups that wait for their
+    // sequence; the merge counters and sequence counters reset themselves
+    REQ(mxs::decode_step_one_launch(c, a->B, a->q), MXS_EUNSUPPORTED,
+        "decode_step_one_launch: needs MXFP4 K / V and index caches, q <= 8 and B x page_table_stride >= 8192 "
+        "(got formats %d / %d, q = %d, %lld pages)", cache->kv_format, cache->idx_format, a->q,
+        (long long)a->B * cache->page_table_stride);
+    mxs::StepStore st;
+    if (store) {
+      st.k_new = a->k_new;
+      st.v_new = a->v_new;
+      st.idx_new = a->idx_new;
+    }
+    st.q_att = a->query;
+    st.q_dtype = a->q_dtype;
+    st.H = a->H;
+    st.q8 = q8;
+    return launched(mxs::launch_decode_step(c, a->q_idx, a->w, a->B, a->q, a->H_I, scores, st, a->H, a->topk, P,
+                                            a->sm_scale, table, sp_m, sp_l, sp_o, fm, seq_cnt, s),
+                    "decode_step_one_launch");
+  }
 
   // 1 - 3: the new rows into the pages, q -> e4m3 and the scores, one launch
   // (the waves that own a page holding new positions store those index rows
@@ -384,14 +425,17 @@ int decode_step(const mxs_step *a, void *ws, size_t ws_bytes, void *stream) {
   // workgroup selects its row's blocks from the scores itself (partition 0
   // writes the row's block table), and the row's last partition to finish
   // merges the row
-  const void *qa = mx ? static_cast<const void *>(q8) : a->query;
-  mxs::FusedMerge fm;
-  fm.counters = counters;
-  fm.out = a->out;
-  fm.lse = a->lse;
   return launched(mxs::launch_select_attn(c, scores, qa, a->B, a->q, a->H, a->topk, P, a->sm_scale, table, sp_m, sp_l,
                                           sp_o, fm, s),
                   "decode_step: top-k + split attention + merge");
+}
+
+int decode_step(const mxs_step *a, void *ws, size_t ws_bytes, void *stream) {
+  return step_entry(a, ws, ws_bytes, stream, false);
+}
+
+int decode_step_one_launch(const mxs_step *a, void *ws, size_t ws_bytes, void *stream) {
+  return step_entry(a, ws, ws_bytes, stream, true);
 }
 
 int decode_step_reuse(const mxs_step *a, const int32_t *block_table, void *ws, size_t ws_bytes, void *stream) {

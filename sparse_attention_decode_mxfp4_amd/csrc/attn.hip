@@ -44,6 +44,7 @@
 #include "topk.hpp"
 #include "merge.hpp"
 #include "mxsparse.h"
+#include "score.hpp"
 
 namespace mxs {
 
@@ -128,16 +129,25 @@ template <int FMT> struct QueryRegs;
 template <> struct QueryRegs<0> { uint2 c[4]; };
 template <> struct QueryRegs<1> { u32x4 c[4]; };
 
-template <int FMT>
+template <int FMT, bool COH = false>
 __device__ __forceinline__ void load_query(const void *__restrict__ qv, int row, int H, int n, int kg,
                                            QueryRegs<FMT> &q) {
   const int64_t base = ((int64_t)row * H + (n < H ? n : 0)) * kDim + 32 * kg;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    if constexpr (FMT == 0)
-      q.c[s] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint8_t *>(qv) + base + 8 * s);
-    else
+    if constexpr (FMT == 0) {
+      const uint8_t *src = reinterpret_cast<const uint8_t *>(qv) + base + 8 * s;
+      if constexpr (COH) {                         // written earlier in the same launch (device-coherent)
+        const uint64_t x = __hip_atomic_load(reinterpret_cast<const uint64_t *>(src), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        q.c[s] = make_uint2((uint32_t)x, (uint32_t)(x >> 32));
+      } else {
+        q.c[s] = *reinterpret_cast<const uint2 *>(src);
+      }
+    } else {
+      static_assert(!COH || FMT == 0, "the single-launch step packs an e4m3 query");
       q.c[s] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(qv) + base + 8 * s);
+    }
   }
 }
 
@@ -453,7 +463,8 @@ __device__ __forceinline__ void write_row(float (&s_m)[NW][16], float (&s_l)[NW]
         reinterpret_cast<uint32_t *>(dst)[0] = packed.x;
         reinterpret_cast<uint32_t *>(dst)[1] = packed.y;
       }
-      if (lse && d == 0) lse[r] = Lsum > 0.0f ? M * kLn2 + __logf(Lsum) : -__builtin_inff();
+      // an explicit fma: the same rounding in every kernel this is inlined into
+      if (lse && d == 0) lse[r] = Lsum > 0.0f ? __builtin_fmaf(M, kLn2, __logf(Lsum)) : -__builtin_inff();
     }
   }
 }
@@ -493,29 +504,51 @@ __global__ __launch_bounds__(256) void k_split_attn(CacheView c, const void *__r
   write_partial<false, kAttnWaves>(s_m, s_l, s_o, m_run, l_run, O, row, H, P, p, sp_m, sp_l, sp_o);
 }
 
-// The decode step's attention. SELECT: the workgroup first selects its row's
-// top-k blocks itself (the workgroup selection of topk.hpp over the row's
-// scores) and partition 0 writes the row's block table; otherwise the row's
-// blocks come from a given block table (a selection reused from an earlier
-// layer; entries < 0, past the table or past the row's position are
-// skipped). The row's page table is staged in LDS. Everything the workgroup
-// needs from memory before the K / V pages — the context length, the score
-// row or table row and the page-table row — is requested in one round trip;
-// the query goes out with the first block's pages.
-template <int FMT, int ITEMS, bool SELECT>
-__global__ __launch_bounds__(64 * kStepWaves) void k_select_attn(CacheView c, const float *__restrict__ scores,
-                                                     const void *__restrict__ qv, int32_t q_rows, int32_t H,
-                                                     int32_t topk, int32_t P, float sm_scale,
-                                                     int32_t *__restrict__ block_table, float *__restrict__ sp_m,
-                                                     float *__restrict__ sp_l, float *__restrict__ sp_o,
-                                                     FusedMerge fm) {
+// Shared memory of one decode-step attention workgroup.
+template <int ITEMS, bool SELECT>
+struct StepAttnSmem {
+  TopkSmem<SELECT ? ITEMS : 1, kStepWaves> tk;
+  int32_t s_pt[64 * kStepWaves * ITEMS];
+  float s_m[kStepWaves][16], s_l[kStepWaves][16];
+  float s_o[kStepWaves][16][kDim + 4];
+  uint32_t s_last;
+};
+
+// What the attention workgroups of the single-launch decode step wait for:
+// the scoring workgroups of their sequence (seq_cnt[2 b] counts them in, up
+// to n_score each) — and once every attention workgroup of the sequence has
+// passed (seq_cnt[2 b + 1] counts them), the last one sets both words back to
+// zero for the next launch. Null in the two-launch step.
+struct StepWait {
+  uint32_t *seq_cnt = nullptr;     // [B][2]
+  uint32_t n_score = 0;            // scoring workgroups per sequence
+};
+
+// Spin limit of the wait (iterations of ~128 clocks each, about a quarter of
+// a second): a bound that every wave reaches even if a count never arrives.
+constexpr uint32_t kWaitSpins = 1u << 21;
+
+// The decode step's attention workgroup (partition p of query row j of
+// sequence b). SELECT: the workgroup first selects its row's top-k blocks
+// itself (the workgroup selection of topk.hpp over the row's scores) and
+// partition 0 writes the row's block table; otherwise the row's blocks come
+// from a given block table (a selection reused from an earlier layer;
+// entries < 0, past the table or past the row's position are skipped). The
+// row's page table is staged in LDS. Everything the workgroup needs from
+// memory before the K / V pages — the context length, the score row or table
+// row and the page-table row — is requested in one round trip; the query goes
+// out with the first block's pages. With a StepWait (the single-launch step)
+// the score row and the query were written earlier in the same launch by
+// other workgroups: the workgroup waits for its sequence's count first and
+// reads them with device-coherent loads.
+template <int FMT, int ITEMS, bool SELECT, bool WAIT>
+__device__ __forceinline__ void step_attn_wg(const CacheView &c, const float *__restrict__ scores,
+                                             const void *__restrict__ qv, int32_t q_rows, int32_t H, int32_t topk,
+                                             int32_t P, float sm_scale, int32_t *__restrict__ block_table,
+                                             float *__restrict__ sp_m, float *__restrict__ sp_l,
+                                             float *__restrict__ sp_o, const FusedMerge &fm, const StepWait &sw,
+                                             int p, int j, int b, StepAttnSmem<ITEMS, SELECT> &sm) {
   constexpr int NT = 64 * kStepWaves;              // threads
-  __shared__ TopkSmem<SELECT ? ITEMS : 1, kStepWaves> tk;
-  __shared__ int32_t s_pt[NT * ITEMS];
-  __shared__ float s_m[kStepWaves][16], s_l[kStepWaves][16];
-  __shared__ float s_o[kStepWaves][16][kDim + 4];
-  __shared__ uint32_t s_last;
-  const int p = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int row = b * q_rows + j;
   const int tid = threadIdx.x, lane = tid & 63;
   const int n = lane & 15, kg = lane >> 4;
@@ -528,19 +561,41 @@ __global__ __launch_bounds__(64 * kStepWaves) void k_select_attn(CacheView c, co
 #pragma unroll
   for (int r = 0; r < ITEMS; ++r) {
     const int i = min(tid + NT * r, stride - 1);   // clamped: unconditional loads
-    if constexpr (SELECT) v[r] = scores[(int64_t)row * stride + i];
+    if constexpr (SELECT && !WAIT) v[r] = scores[(int64_t)row * stride + i];
     pt[r] = c.page_table[(int64_t)b * stride + i];
   }
   if constexpr (!SELECT) given = block_table[(int64_t)row * topk + min(lane, topk - 1)];
+  if constexpr (WAIT) {
+    // the sequence's scores, new K / V rows and e4m3 query are complete once
+    // all its scoring workgroups have counted in
+    if (tid == 0) {
+      uint32_t spins = 0;
+      while (__hip_atomic_load(sw.seq_cnt + 2 * b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < sw.n_score &&
+             ++spins < kWaitSpins)
+        __builtin_amdgcn_s_sleep(2);
+      // every attention workgroup of the sequence past the wait: reset both words
+      if (__hip_atomic_fetch_add(sw.seq_cnt + 2 * b + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+          (uint32_t)(q_rows * P - 1)) {
+        __hip_atomic_store(sw.seq_cnt + 2 * b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(sw.seq_cnt + 2 * b + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < ITEMS; ++r) {
+      const int i = min(tid + NT * r, stride - 1);
+      v[r] = __hip_atomic_load(scores + (int64_t)row * stride + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   const int pos = L - q_rows + j;
 #pragma unroll
   for (int r = 0; r < ITEMS; ++r)
-    if (tid + NT * r < stride) s_pt[tid + NT * r] = pt[r];
+    if (tid + NT * r < stride) sm.s_pt[tid + NT * r] = pt[r];
   int n_sel;
   uint32_t sel;
   if constexpr (SELECT) {
     const int n_cand = pos < 0 ? 0 : min(pos / kTokens + 1, stride);
-    sel = wg_topk<ITEMS, kStepWaves>(v, n_cand, topk, tk, n_sel);
+    sel = wg_topk<ITEMS, kStepWaves>(v, n_cand, topk, sm.tk, n_sel);
     lds_barrier();                                 // s_pt (the selection may return before any barrier)
     if (p == 0 && tid < topk) block_table[(int64_t)row * topk + tid] = tid < n_sel ? (int32_t)sel : -1;
   } else {
@@ -552,7 +607,7 @@ __global__ __launch_bounds__(64 * kStepWaves) void k_select_attn(CacheView c, co
   const int cps = (topk + P - 1) / P;
   const int slot0 = p * cps, slot1 = min(slot0 + cps, n_sel);
   QueryRegs<FMT> qr;                               // widened after the first block's pages are requested
-  load_query<FMT>(qv, row, H, n, kg, qr);
+  load_query<FMT, WAIT>(qv, row, H, n, kg, qr);
   float m_run = -__builtin_inff(), l_run = 0.0f;
   f32x4 O[8];
 #pragma unroll
@@ -565,14 +620,14 @@ __global__ __launch_bounds__(64 * kStepWaves) void k_select_attn(CacheView c, co
         return (blk < 0 || blk >= stride || blk * kTokens > pos) ? -1 : blk;
       },
       [&](int blk) {
-        const int phys = __builtin_amdgcn_readfirstlane(s_pt[blk]);
+        const int phys = __builtin_amdgcn_readfirstlane(sm.s_pt[blk]);
         return (phys < 0 || phys >= c.num_pages) ? -1 : phys;
       });
   if (P == 1) {                                     // the row is this workgroup's alone: no exchange
-    write_row<kStepWaves>(s_m, s_l, s_o, m_run, l_run, O, row, H, fm.out, fm.lse);
+    write_row<kStepWaves>(sm.s_m, sm.s_l, sm.s_o, m_run, l_run, O, row, H, fm.out, fm.lse);
     return;
   }
-  write_partial<true, kStepWaves>(s_m, s_l, s_o, m_run, l_run, O, row, H, P, p, sp_m, sp_l, sp_o);
+  write_partial<true, kStepWaves>(sm.s_m, sm.s_l, sm.s_o, m_run, l_run, O, row, H, P, p, sp_m, sp_l, sp_o);
 
   // ---- the row's merge, by its last partition workgroup to finish. The
   // partials went out as agent-scope (device-coherent) stores; once every
@@ -583,12 +638,107 @@ __global__ __launch_bounds__(64 * kStepWaves) void k_select_attn(CacheView c, co
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();
   if (tid == 0)
-    s_last = __hip_atomic_fetch_add(fm.counters + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (uint32_t)(P - 1);
+    sm.s_last = __hip_atomic_fetch_add(fm.counters + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (uint32_t)(P - 1);
   lds_barrier();
-  if (!s_last) return;
+  if (!sm.s_last) return;
   if (tid == 0) fm.counters[row] = 0u;            // every arrival is in: the row's counter is free for the next launch
   merge_row(sp_m, sp_l, sp_o, row, H, P, fm.out, fm.lse);
+}
+
+template <int FMT, int ITEMS, bool SELECT>
+__global__ __launch_bounds__(64 * kStepWaves) void k_select_attn(CacheView c, const float *__restrict__ scores,
+                                                     const void *__restrict__ qv, int32_t q_rows, int32_t H,
+                                                     int32_t topk, int32_t P, float sm_scale,
+                                                     int32_t *__restrict__ block_table, float *__restrict__ sp_m,
+                                                     float *__restrict__ sp_l, float *__restrict__ sp_o,
+                                                     FusedMerge fm) {
+  __shared__ StepAttnSmem<ITEMS, SELECT> sm;
+  step_attn_wg<FMT, ITEMS, SELECT, false>(c, scores, qv, q_rows, H, topk, P, sm_scale, block_table, sp_m, sp_l, sp_o,
+                                          fm, StepWait{}, blockIdx.x, blockIdx.y, blockIdx.z, sm);
+}
+
+// ---------------------------------------------------------------- the step as one launch
+// The whole decode step in one grid: the scoring workgroups first (ids below
+// B ny: sequence id % B, wave group id / B, the two-launch scorer's 4-wave x
+// 8-page x 3-stage shape), then the attention workgroups (partition, row,
+// sequence). A scoring workgroup writes its scores, its share of the step's
+// K / V rows and of the e4m3 query with device-coherent stores, waits for
+// them to complete and counts itself in for its sequence. An attention
+// workgroup loads its context length and page-table row, waits for its
+// sequence's count, then selects, attends and merges as in the two-launch
+// step. Workgroups are dispatched in increasing id order on each XCD, so an
+// attention workgroup only ever waits for scoring workgroups that were
+// dispatched before it, and those wait for nothing: the wait always ends, and
+// it is also bounded (kWaitSpins). Attention workgroups of a sequence start
+// as soon as the CUs that scored free up, so their launch and prologue
+// overlap the rest of the scan instead of following it.
+template <int MT, int ITEMS>
+constexpr int kStepLds = kScoreLds<MT, 0, 4, 3> > (int)sizeof(StepAttnSmem<ITEMS, true>)
+                             ? kScoreLds<MT, 0, 4, 3>
+                             : (int)sizeof(StepAttnSmem<ITEMS, true>);
+
+template <int MT, int ITEMS>
+__global__ __launch_bounds__(64 * kStepWaves) void k_decode_step(
+    CacheView c, const uint16_t *__restrict__ q_idx, const float *__restrict__ w, int32_t q, int32_t H_I,
+    float *__restrict__ scores, StepStore st, int32_t B, int32_t ny, int32_t H, int32_t topk, int32_t P,
+    float sm_scale, int32_t *__restrict__ block_table, float *__restrict__ sp_m, float *__restrict__ sp_l,
+    float *__restrict__ sp_o, FusedMerge fm, StepWait sw) {
+  // one LDS object, used by either role
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kStepLds<MT, ITEMS>];
+  const int n_score = B * ny;
+  if ((int)blockIdx.x < n_score) {
+    const int b = (int)blockIdx.x % B, gy = (int)blockIdx.x / B;
+    index_score_wg<MT, 0, 4, 8, 3, true>(c, q_idx, w, q, H_I, scores, st, b, gy, ny, lds);
+    // every store of this workgroup done (vmcnt counts stores too), then one
+    // arrival for the sequence
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(sw.seq_cnt + 2 * b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  const int a = (int)blockIdx.x - n_score;
+  const int p = a % P, j = (a / P) % q, b = a / (P * q);
+  step_attn_wg<0, ITEMS, true, true>(c, scores, st.q8, q, H, topk, P, sm_scale, block_table, sp_m, sp_l, sp_o, fm,
+                                     sw, p, j, b, *reinterpret_cast<StepAttnSmem<ITEMS, true> *>(lds));
+}
+
+bool decode_step_one_launch(const CacheView &c, int32_t B, int32_t q) {
+  return c.kv_format == 0 && c.idx_format == 0 && q <= 8 && (int64_t)B * c.stride >= 256 * 32;
+}
+
+template <int MT>
+static void launch_step_mt(const CacheView &c, const uint16_t *q_idx, const float *w, int32_t B, int32_t q,
+                           int32_t H_I, float *scores, const StepStore &st, int32_t H, int32_t topk, int32_t P,
+                           float sm_scale, int32_t *block_table, float *sp_m, float *sp_l, float *sp_o,
+                           const FusedMerge &fm, uint32_t *seq_cnt, hipStream_t s) {
+  constexpr int NT = 64 * kStepWaves;
+  const int ny = (c.stride + 32 - 1) / 32;         // 4 waves x 8 pages per scoring workgroup
+  StepWait sw;
+  sw.seq_cnt = seq_cnt;
+  sw.n_score = (uint32_t)ny;
+  const dim3 grid((unsigned)(B * ny + B * q * P)), block(NT);
+#define MXS_STEP(I)                                                                                           \
+  hipLaunchKernelGGL((k_decode_step<MT, I>), grid, block, 0, s, c, q_idx, w, q, H_I, scores, st, B, ny, H, topk, \
+                     P, sm_scale, block_table, sp_m, sp_l, sp_o, fm, sw)
+  if (c.stride <= NT * 2) MXS_STEP(2);
+  else if (c.stride <= NT * 8) MXS_STEP(8);
+  else MXS_STEP(32);
+#undef MXS_STEP
+}
+
+hipError_t launch_decode_step(const CacheView &c, const uint16_t *q_idx, const float *w, int32_t B, int32_t q,
+                              int32_t H_I, float *scores, const StepStore &st, int32_t H, int32_t topk, int32_t P,
+                              float sm_scale, int32_t *block_table, float *sp_m, float *sp_l, float *sp_o,
+                              const FusedMerge &fm, uint32_t *seq_cnt, hipStream_t s) {
+  if (B * q == 0) return hipSuccess;
+  if (q <= 4)
+    launch_step_mt<1>(c, q_idx, w, B, q, H_I, scores, st, H, topk, P, sm_scale, block_table, sp_m, sp_l, sp_o, fm,
+                      seq_cnt, s);
+  else
+    launch_step_mt<2>(c, q_idx, w, B, q, H_I, scores, st, H, topk, P, sm_scale, block_table, sp_m, sp_l, sp_o, fm,
+                      seq_cnt, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_split_attn(const CacheView &c, const void *q, int q_dtype, const int32_t *block_table,

@@ -101,6 +101,40 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t d) {
                     bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, true)));
 }
 
+// ---------------------------------------------------------------- stores seen across the GPU
+// COH: a store that other workgroups of the same launch, on any XCD, read
+// after a device-scope counter says it is done (an agent-scope relaxed atomic
+// store: the sc1 cache policy, so the value does not wait in this XCD's L2);
+// otherwise a plain store (read only by later launches).
+template <bool COH>
+__device__ __forceinline__ void st_u8(uint8_t *p, uint32_t v) {
+  if constexpr (COH)
+    __hip_atomic_store(p, (uint8_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = (uint8_t)v;
+}
+template <bool COH>
+__device__ __forceinline__ void st_u16(uint16_t *p, uint32_t v) {
+  if constexpr (COH)
+    __hip_atomic_store(p, (uint16_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = (uint16_t)v;
+}
+template <bool COH>
+__device__ __forceinline__ void st_u32(uint32_t *p, uint32_t v) {
+  if constexpr (COH)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+template <bool COH>
+__device__ __forceinline__ void st_f32(float *p, float v) {
+  if constexpr (COH)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+
 // ---------------------------------------------------------------- wave helpers
 // The value lane (lane ^ M) holds, for M a power of two below 64:
 //   1, 2: DPP quad permutes; 8: row rotate by 8; 4: row rotates by 4 and 12

@@ -15,6 +15,9 @@ struct CacheView {
   const int32_t *context_lens;
 };
 
+// n words at p set to zero (store.hip)
+hipError_t launch_zero(uint32_t *p, size_t n, hipStream_t s);
+
 // row store / q store (store.hip)
 hipError_t launch_row_store(int format, const float *rows, int64_t n, const int64_t *slots,
                             uint8_t *pages, int32_t num_pages, hipStream_t s);
@@ -68,6 +71,18 @@ hipError_t launch_select_attn(const CacheView &c, const float *scores, const voi
 hipError_t launch_table_attn(const CacheView &c, const int32_t *block_table, const void *q, int32_t B, int32_t q_rows,
                              int32_t H, int32_t topk, int32_t P, float sm_scale, float *sp_m, float *sp_l, float *sp_o,
                              const FusedMerge &fm, hipStream_t s);
+
+// the whole decode step as one launch (attn.hip): scoring workgroups (which
+// also do the step's row and query stores, device-coherent) and then
+// attention workgroups that wait for their sequence's scores. Taken when
+// decode_step_one_launch holds (MXFP4 K / V and index caches, q <= 8 query
+// rows, B x page_table_stride >= 8192 pages); seq_cnt [B][2] zero on entry and
+// left zero; st.counters must be null (the merge counters reset themselves).
+bool decode_step_one_launch(const CacheView &c, int32_t B, int32_t q);
+hipError_t launch_decode_step(const CacheView &c, const uint16_t *q_idx, const float *w, int32_t B, int32_t q,
+                              int32_t H_I, float *scores, const StepStore &st, int32_t H, int32_t topk, int32_t P,
+                              float sm_scale, int32_t *block_table, float *sp_m, float *sp_l, float *sp_o,
+                              const FusedMerge &fm, uint32_t *seq_cnt, hipStream_t s);
 
 // streaming read of every index page in page-table order (read.hip): a
 // measurement of the scan's bandwidth ceiling; sink receives at most one word

@@ -38,17 +38,19 @@ __device__ __forceinline__ uint32_t mx_scale_word(uint32_t sb) {
          ((uint32_t)__builtin_amdgcn_readlane((int)sb, 48) << 24);
 }
 
-// The quantized row into token `tok` of the MXFP4 page at `page`.
+// The quantized row into token `tok` of the MXFP4 page at `page` (COH: see st_u8).
+template <bool COH = false>
 __device__ __forceinline__ void mx_write_row(uint32_t code, uint32_t sb, uint8_t *page, int tok, int lane) {
-  page[64 * tok + lane] = (uint8_t)code;
-  if (lane == 0)
-    *reinterpret_cast<uint32_t *>(page + kMxScaleOff + 4 * tok) = mx_scale_word(sb);
+  st_u8<COH>(page + 64 * tok + lane, code);
+  const uint32_t word = mx_scale_word(sb);
+  if (lane == 0) st_u32<COH>(reinterpret_cast<uint32_t *>(page + kMxScaleOff + 4 * tok), word);
 }
 
+template <bool COH = false>
 __device__ __forceinline__ void mx_store_row(float2 x, uint8_t *page, int tok, int lane) {
   uint32_t code, sb;
   mx_quant_row(x, code, sb);
-  mx_write_row(code, sb, page, tok, lane);
+  mx_write_row<COH>(code, sb, page, tok, lane);
 }
 
 // FP8 per-token row: scale = fp32(amax / 448) (1 for an all-zero row),
@@ -67,12 +69,13 @@ __device__ __forceinline__ void f8_quant_row(float2 x, uint32_t &codes, float &s
   codes = e4m3_code(x.x / scale) | (e4m3_code(x.y / scale) << 8);
 }
 
+template <bool COH = false>
 __device__ __forceinline__ void f8_store_row(float2 x, uint8_t *page, int tok, int lane) {
   uint32_t codes;
   float scale;
   f8_quant_row(x, codes, scale);
-  *reinterpret_cast<uint16_t *>(page + 128 * tok + 2 * lane) = (uint16_t)codes;
-  if (lane == 0) *reinterpret_cast<float *>(page + kF8ScaleOff + 4 * tok) = scale;
+  st_u16<COH>(reinterpret_cast<uint16_t *>(page + 128 * tok + 2 * lane), codes);
+  if (lane == 0) st_f32<COH>(reinterpret_cast<float *>(page + kF8ScaleOff + 4 * tok), scale);
 }
 
 __device__ __forceinline__ float load_q_elem(const void *q, int q_dtype, int64_t i) {

@@ -12,6 +12,8 @@
 // One wave stores one 128-element row: lane l owns elements 2l and 2l+1, so a
 // 32-element group is 16 lanes and its amax is a 16-lane reduction; the wave
 // writes the row's 64 data bytes (one per lane) and one dword of 4 scales.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "rowstore.hpp"
@@ -102,6 +104,17 @@ __global__ __launch_bounds__(256) void k_reuse_store(CacheView c, const float *_
                  (e4m3_code(v[4 * k + 3]) << 24);
     *reinterpret_cast<u32x4 *>(q8 + e0) = codes;        // q8: the step workspace, 16-byte aligned
   }
+}
+
+__global__ __launch_bounds__(256) void k_zero(uint32_t *__restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
+hipError_t launch_zero(uint32_t *p, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = std::min<size_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_reuse_store(const CacheView &c, const float *k_new, const float *v_new, const void *q, int q_dtype,

@@ -29,16 +29,21 @@ def mx():
 
 def _setup(name):
     import workloads.gpu as WG
-    inp = W.make_inputs(W.WORKLOADS[name].with_(B=4))
+    if name == "one_launch":       # 4 x 2048-entry page tables, through decode_step_one_launch
+        wl = W.WORKLOADS["mxfp4_65k"].with_(name="one_launch", table_stride=2048)
+    else:
+        wl = W.WORKLOADS[name].with_(B=4)
+    inp = W.make_inputs(wl)
     pools = WG.fill_prefix(inp, WG.empty_pools(inp))
     return inp, WG.make_cache(inp, pools), WG.step_tensors(inp)
 
 
-@pytest.mark.parametrize("name", ["mxfp4_65k", "fp8"])
+@pytest.mark.parametrize("name", ["mxfp4_65k", "fp8", "one_launch"])
 def test_decode_step_graph_replays_equal_eager(mx, name):
     inp, cache, t = _setup(name)
     wl = inp.wl
     kw = dict(k_new=t.get("k_new"), v_new=t.get("v_new"), idx_new=t.get("idx_new"))
+    kw["one_launch"] = name == "one_launch"
     step = mx.DecodeStep(cache, t["query"], t["q_idx"], t["w"], wl.topk, wl.sm_scale, **kw)
     other_q = (t["query"].float() * 0.5 - 0.25).to(t["query"].dtype).contiguous()
     other = mx.DecodeStep(cache, other_q, t["q_idx"], t["w"], wl.topk, wl.sm_scale, **kw)

@@ -85,19 +85,24 @@ def test_reuse_step_small(mx, name):
     check_reuse(inp, g, table, range(inp.wl.B))
 
 
-@pytest.mark.parametrize("name", ["tiny", "fp8", "mxfp4_65k"])
+@pytest.mark.parametrize("name", ["tiny", "fp8", "mxfp4_65k", "one_launch"])
 def test_reuse_step_on_the_full_steps_selection_is_bitwise_the_full_step(mx, name):
     """decode_step, then decode_step_reuse over the block table it wrote, from
-    the same pre-step caches: identical output, lse and K / V pages."""
+    the same pre-step caches: identical output, lse and K / V pages (also after
+    decode_step_one_launch over 2048-entry page tables)."""
     import workloads.gpu as WG
-    inp = W.make_inputs(W.WORKLOADS[name])
+    if name == "one_launch":
+        inp = W.make_inputs(W.WORKLOADS["mxfp4_65k"].with_(name="one_launch", table_stride=2048))
+    else:
+        inp = W.make_inputs(W.WORKLOADS[name])
     wl = inp.wl
     pools = WG.fill_prefix(inp, WG.empty_pools(inp))
     cache = WG.make_cache(inp, pools)
     t = WG.step_tensors(inp)
     table = torch.empty((wl.B, wl.q, wl.topk), dtype=torch.int32, device="cuda")
     full = mx.DecodeStep(cache, t["query"], t["q_idx"], t["w"], wl.topk, wl.sm_scale, k_new=t.get("k_new"),
-                         v_new=t.get("v_new"), idx_new=t.get("idx_new"), block_table_out=table)
+                         v_new=t.get("v_new"), idx_new=t.get("idx_new"), block_table_out=table,
+                         one_launch=name == "one_launch")
     full.run()
     torch.cuda.synchronize()
     g = run_reuse(mx, inp, table.cpu().numpy())
@@ -170,7 +175,7 @@ def test_reuse_step_alternating_tables_share_a_workspace(mx):
     cache = WG.make_cache(inp, pools)
     t = WG.step_tensors(inp)
     nb = mx.workspace_bytes(wl.B, wl.q, wl.H, 1, wl.topk, cache.stride)
-    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
     tabs = [torch.from_numpy(random_table(inp, s).astype(np.int32)).cuda() for s in (1, 2)]
     steps = [mx.DecodeStepReuse(cache, t["query"], tb, wl.sm_scale, k_new=t.get("k_new"), v_new=t.get("v_new"),
                                 ws=ws) for tb in tabs]

@@ -210,7 +210,15 @@ def test_decode_step_fp8_65k(mx):
     check_step(inp, g, range(inp.wl.B))
 
 
-@pytest.mark.parametrize("name", ["mxfp4_65k", "fp8"])
+# "one_launch": the 65K workload with 2048-entry page tables (B x stride =
+# 8192 pages, which decode_step_one_launch takes) run through that entry point
+def _wl(name):
+    if name == "one_launch":
+        return W.WORKLOADS["mxfp4_65k"].with_(name="one_launch", table_stride=2048)
+    return W.WORKLOADS[name].with_(B=4)
+
+
+@pytest.mark.parametrize("name", ["mxfp4_65k", "fp8", "one_launch"])
 def test_decode_step_repeats_bit_exact(mx, name):
     """The same step run many times gives bit-identical output and lse: each
     row is merged by whichever of its partition workgroups finishes last, from
@@ -218,13 +226,14 @@ def test_decode_step_repeats_bit_exact(mx, name):
     so any partial not yet visible to the merging workgroup would show as a
     difference. Also checked against the oracle once."""
     import workloads.gpu as WG
-    inp = W.make_inputs(W.WORKLOADS[name].with_(B=4))
+    inp = W.make_inputs(_wl(name))
     wl = inp.wl
     pools = WG.fill_prefix(inp, WG.empty_pools(inp))
     cache = WG.make_cache(inp, pools)
     t = WG.step_tensors(inp)
     step = mx.DecodeStep(cache, t["query"], t["q_idx"], t["w"], wl.topk, wl.sm_scale,
-                         k_new=t.get("k_new"), v_new=t.get("v_new"), idx_new=t.get("idx_new"))
+                         k_new=t.get("k_new"), v_new=t.get("v_new"), idx_new=t.get("idx_new"),
+                         one_launch=name == "one_launch")
     step.run()
     torch.cuda.synchronize()
     out0, lse0 = step.out.clone(), step.lse.clone()
@@ -237,22 +246,23 @@ def test_decode_step_repeats_bit_exact(mx, name):
         PT.check_attention(O[b], r["O"][b], f"{name} b={b}")
 
 
-@pytest.mark.parametrize("name", ["mxfp4_65k", "fp8"])
+@pytest.mark.parametrize("name", ["mxfp4_65k", "fp8", "one_launch"])
 def test_decode_step_alternating_inputs_share_a_workspace(mx, name):
     """Two steps with different queries run alternately on one workspace: each
     run's output and lse equal its own first run bit for bit, so no merge ever
     reads a partial left in the workspace (or in a cache) by the other step's
     previous run."""
     import workloads.gpu as WG
-    inp = W.make_inputs(W.WORKLOADS[name].with_(B=4))
+    inp = W.make_inputs(_wl(name))
     wl = inp.wl
     pools = WG.fill_prefix(inp, WG.empty_pools(inp))
     cache = WG.make_cache(inp, pools)
     t = WG.step_tensors(inp)
     qb = (t["query"].float() * -0.75 + 0.5).to(t["query"].dtype).contiguous()
     nb = mx.workspace_bytes(wl.B, wl.q, wl.H, wl.H_I, wl.topk, cache.stride)
-    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
-    kw = dict(k_new=t.get("k_new"), v_new=t.get("v_new"), idx_new=t.get("idx_new"), ws=ws)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    kw = dict(k_new=t.get("k_new"), v_new=t.get("v_new"), idx_new=t.get("idx_new"), ws=ws,
+              one_launch=name == "one_launch")
     steps = [mx.DecodeStep(cache, q, t["q_idx"], t["w"], wl.topk, wl.sm_scale, **kw) for q in (t["query"], qb)]
     first = []
     for s_ in steps:
@@ -276,7 +286,7 @@ def test_decode_step_workspace_needs_no_initialization(mx, name):
     its merge counters itself): a workspace filled with 0xFF or 0x01 bytes
     gives the output and lse of a zero-filled one, bit for bit."""
     import workloads.gpu as WG
-    inp = W.make_inputs(W.WORKLOADS[name].with_(B=4))
+    inp = W.make_inputs(_wl(name))
     wl = inp.wl
     pools = WG.fill_prefix(inp, WG.empty_pools(inp))
     cache = WG.make_cache(inp, pools)
@@ -293,3 +303,74 @@ def test_decode_step_workspace_needs_no_initialization(mx, name):
         res.append((s_.out.clone(), s_.lse.clone()))
     for k in (1, 2):
         assert torch.equal(res[k][0], res[0][0]) and torch.equal(res[k][1], res[0][1]), f"fill {k}"
+
+
+def test_one_launch_workspace_init(mx):
+    """decode_step_one_launch over a workspace filled with 0xFF or 0x01 bytes
+    and then zeroed by mxs_workspace_init gives the output and lse of a freshly
+    zeroed one, bit for bit; each call leaves the workspace ready for the next
+    (a second call without re-zeroing gives the same again)."""
+    import workloads.gpu as WG
+    inp = W.make_inputs(_wl("one_launch"))
+    wl = inp.wl
+    pools = WG.fill_prefix(inp, WG.empty_pools(inp))
+    cache = WG.make_cache(inp, pools)
+    t = WG.step_tensors(inp)
+    nb = mx.workspace_bytes(wl.B, wl.q, wl.H, wl.H_I, wl.topk, cache.stride)
+    res = []
+    for fill in (0x00, 0xFF, 0x01):
+        ws = torch.full((nb,), fill, dtype=torch.uint8, device="cuda")
+        mx.workspace_init(ws)
+        s_ = mx.DecodeStep(cache, t["query"], t["q_idx"], t["w"], wl.topk, wl.sm_scale, k_new=t.get("k_new"),
+                           v_new=t.get("v_new"), idx_new=t.get("idx_new"), ws=ws, one_launch=True)
+        for _ in range(2):
+            s_.run()
+            torch.cuda.synchronize()
+            res.append((s_.out.clone(), s_.lse.clone()))
+    for k in range(1, len(res)):
+        assert torch.equal(res[k][0], res[0][0]) and torch.equal(res[k][1], res[0][1]), f"run {k}"
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("headline", {}), ("long", dict(table_stride=2048)), ("b32", {}),               # ragged contexts
+    ("mxfp4_65k", dict(name="wide", table_stride=4096)),                              # 32 candidates per thread
+    ("mxfp4_65k", dict(name="straddle", B=4, ctx_rule=("list", (262144, 4100, 8196, 65540)), topk=32)),
+])
+def test_one_launch_equals_two_launches(mx, name, kw):
+    """decode_step_one_launch gives decode_step's output, lse, block table and
+    K / V / index pages bit for bit (the same device code for every stage;
+    decode_step itself is checked against the oracle above)."""
+    import workloads.gpu as WG
+    inp = W.make_inputs(W.WORKLOADS[name].with_(**kw) if kw else W.WORKLOADS[name])
+    wl = inp.wl
+    res = []
+    for one in (False, True):
+        pools = WG.fill_prefix(inp, WG.empty_pools(inp))
+        cache = WG.make_cache(inp, pools)
+        t = WG.step_tensors(inp)
+        table = torch.empty((wl.B, wl.q, wl.topk), dtype=torch.int32, device="cuda")
+        s_ = mx.DecodeStep(cache, t["query"], t["q_idx"], t["w"], wl.topk, wl.sm_scale, k_new=t.get("k_new"),
+                           v_new=t.get("v_new"), idx_new=t.get("idx_new"), block_table_out=table, one_launch=one)
+        s_.run()
+        torch.cuda.synchronize()
+        res.append((s_.out.clone(), s_.lse.clone(), table.clone(), {k: p.clone() for k, p in pools.items()}))
+        del pools, cache
+    (o0, l0, t0, p0), (o1, l1, t1, p1) = res
+    assert torch.equal(t0, t1), "block tables differ"
+    assert torch.equal(o0, o1) and torch.equal(l0, l1), "output or lse differs"
+    for k in p0:
+        assert torch.equal(p0[k], p1[k]), f"{k} pages differ"
+
+
+def test_one_launch_refuses_unsupported(mx):
+    """FP8 caches (or fewer than 8192 pages) are refused before any launch."""
+    import workloads.gpu as WG
+    inp = W.make_inputs(W.WORKLOADS["fp8"])
+    wl = inp.wl
+    pools = WG.fill_prefix(inp, WG.empty_pools(inp))
+    cache = WG.make_cache(inp, pools)
+    t = WG.step_tensors(inp)
+    s_ = mx.DecodeStep(cache, t["query"], t["q_idx"], t["w"], wl.topk, wl.sm_scale, one_launch=True)
+    with pytest.raises(mx.MxsError) as e:
+        s_.run()
+    assert e.value.status == mx.MXS_EUNSUPPORTED and "one_launch" in str(e.value)
