@@ -14,6 +14,21 @@ an FP8 K/V and index cache in 128-token blocks; vLLM PR #60528, Details): e4m3 e
 a per-token fp32 scale. Reading (parity unpinned, the pages give no rule):
 scale = fp32(amax / 448), 1.0 for an all-zero row, code = e4m3(fp32(x / scale)).
 
+NVFP4 (ATOM PR #2686, timeline entry #2744, "FP4 index cache and NVFP4 sparse
+KV cache"; ATOM PR #2812, commit messages of the MXFP4 index-cache and main-KV
+commits, where NVFP4 K/V and index caches are named and refused). The pages
+name the format without defining it. Reading (parity unpinned against the
+pages' own writer, which is not available): the public NVFP4 description of
+e2m1 elements in 16-element blocks, each block scaled by an e4m3 factor, under
+a second-level fp32 scale. Here that second level is one per token, kept in the page
+(as the FP8 cache keeps its per-token scale), so that a row can be written
+alone. Quantizer, every step an IEEE fp32 operation:
+  amax = max |x|;  S = 1 if amax == 0, else max(amax / 2688, 2^-149)
+  (2688 = 6 * 448: the largest e2m1 value times the largest e4m3 value);
+  block b: c_b = e4m3(a_b / (6 S)), a_b its largest magnitude;
+  d_b = e4m3_value(c_b) * S;  element code = e2m1(x / d_b), 0 when d_b == 0.
+Decoded value: e2m1_value(code) * e4m3_value(c_b) * S (exact in float64).
+
 e4m3 q store (ATOM PR #2812, commit message of the e4m3 q store, and the one
 that factors out ``pack_q_e4m3``): unit scale, round to nearest even, values
 beyond +-448 and +-inf saturate to +-448, NaN stays NaN.
@@ -29,6 +44,10 @@ pages' own writer, which is not available; oracle and library agree on it.
 
   FP8 page (16896 B): token t's 128 e4m3 codes at [128 t, 128 t + 128); token
   t's fp32 scale (little endian) at 16384 + 4 t.
+
+  NVFP4 page (9728 B): token t's codes at [64 t, 64 t + 64) as in the MXFP4
+  page; token t's eight e4m3 block scales (elements 16 b .. 16 b + 15) at
+  8192 + 8 t + b; token t's fp32 scale (little endian) at 9216 + 4 t.
 """
 from __future__ import annotations
 
@@ -44,6 +63,10 @@ MXFP4_PAGE_BYTES = TOKENS * DIM // 2 + TOKENS * (DIM // GROUP)   # 8192 + 512
 MXFP4_SCALE_OFFSET = TOKENS * DIM // 2
 FP8_PAGE_BYTES = TOKENS * DIM + TOKENS * 4                        # 16384 + 512
 FP8_SCALE_OFFSET = TOKENS * DIM
+NV_BLOCK = 16
+NVFP4_PAGE_BYTES = TOKENS * DIM // 2 + TOKENS * (DIM // NV_BLOCK) + TOKENS * 4   # 8192 + 1024 + 512
+NVFP4_BSCALE_OFFSET = TOKENS * DIM // 2
+NVFP4_TSCALE_OFFSET = NVFP4_BSCALE_OFFSET + TOKENS * (DIM // NV_BLOCK)
 
 
 # --------------------------------------------------------------------------
@@ -177,6 +200,42 @@ def fp8_quantize_rows(x: np.ndarray):
 
 
 # --------------------------------------------------------------------------
+# NVFP4 (reading, see the module docstring): e2m1 in 16-element blocks, e4m3
+# block scales, a per-token fp32 scale.
+# --------------------------------------------------------------------------
+_F32_TINY = np.float32(2.0 ** -149)        # the smallest positive fp32 (a subnormal)
+
+
+def nvfp4_quantize_rows(x: np.ndarray):
+    """Quantize fp32 rows [N][128] to (codes uint8 [N][128], block scale codes
+    uint8 [N][8], token scales fp32 [N]); each step in fp32 as the reading
+    states (numpy's float32 operations round as IEEE fp32 does)."""
+    x = np.asarray(x, dtype=np.float32)
+    N = x.shape[0]
+    a = np.abs(x)
+    amax = a.max(axis=1)
+    with np.errstate(divide="ignore", invalid="ignore", under="ignore"):
+        S = np.where(amax == 0, np.float32(1.0),
+                     np.maximum(amax / np.float32(2688.0), _F32_TINY)).astype(np.float32)
+        ab = a.reshape(N, DIM // NV_BLOCK, NV_BLOCK).max(axis=2)                    # [N][8]
+        six_s = (np.float32(6.0) * S).astype(np.float32)
+        cb = e4m3_encode((ab / six_s[:, None]).astype(np.float32))                  # block scale codes
+        d = (E4M3_TABLE[cb.astype(np.int64)].astype(np.float32) * S[:, None]).astype(np.float32)
+        xb = x.reshape(N, DIM // NV_BLOCK, NV_BLOCK)
+        v = (xb / d[:, :, None]).astype(np.float32)
+    codes = np.where(d[:, :, None] > 0, e2m1_encode(np.where(d[:, :, None] > 0, v, 0.0)), 0).astype(np.uint8)
+    return codes.reshape(N, DIM), cb.astype(np.uint8), S
+
+
+def nvfp4_dequantize(codes: np.ndarray, cb: np.ndarray, S: np.ndarray) -> np.ndarray:
+    """e2m1 value times its block's e4m3 value times the token scale, in float64."""
+    N = codes.shape[0]
+    vals = E2M1_TABLE[codes.astype(np.int64)].reshape(N, DIM // NV_BLOCK, NV_BLOCK)
+    sc = E4M3_TABLE[cb.astype(np.int64)] * np.asarray(S, dtype=np.float64)[:, None]
+    return (vals * sc[:, :, None]).reshape(N, DIM)
+
+
+# --------------------------------------------------------------------------
 # Page stores and reads. ``pool`` is a flat uint8 array of num_pages pages.
 # --------------------------------------------------------------------------
 def _page_runs(page_table_row: np.ndarray, t: np.ndarray):
@@ -242,6 +301,33 @@ def fp8_read(pool: np.ndarray, page_table_row: np.ndarray, L: int, positions=Non
     return E4M3_TABLE[codes.astype(np.int64)] * scale[:, None]
 
 
-PAGE_BYTES = {"mxfp4": MXFP4_PAGE_BYTES, "fp8": FP8_PAGE_BYTES}
-STORE = {"mxfp4": mxfp4_store, "fp8": fp8_store}
-READ = {"mxfp4": mxfp4_read, "fp8": fp8_read}
+def nvfp4_store(pool: np.ndarray, page_table_row: np.ndarray, t0: int, rows: np.ndarray) -> None:
+    codes, cb, S = nvfp4_quantize_rows(rows)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)       # [N][64]
+    sb = S.astype("<f4").view(np.uint8).reshape(-1, 4)
+    pages = pool.reshape(-1, NVFP4_PAGE_BYTES)
+    for r, page, off in _page_runs(page_table_row, np.arange(t0, t0 + rows.shape[0])):
+        pages[page, :NVFP4_BSCALE_OFFSET].reshape(TOKENS, 64)[off] = packed[r]
+        pages[page, NVFP4_BSCALE_OFFSET:NVFP4_TSCALE_OFFSET].reshape(TOKENS, DIM // NV_BLOCK)[off] = cb[r]
+        pages[page, NVFP4_TSCALE_OFFSET:].reshape(TOKENS, 4)[off] = sb[r]
+
+
+def nvfp4_read(pool: np.ndarray, page_table_row: np.ndarray, L: int, positions=None) -> np.ndarray:
+    t = np.arange(L) if positions is None else np.asarray(positions, dtype=np.int64)
+    packed = np.empty((t.size, 64), dtype=np.uint8)
+    cb = np.empty((t.size, DIM // NV_BLOCK), dtype=np.uint8)
+    sb = np.empty((t.size, 4), dtype=np.uint8)
+    pages = pool.reshape(-1, NVFP4_PAGE_BYTES)
+    for r, page, off in _page_runs(page_table_row, t):
+        packed[r] = pages[page, :NVFP4_BSCALE_OFFSET].reshape(TOKENS, 64)[off]
+        cb[r] = pages[page, NVFP4_BSCALE_OFFSET:NVFP4_TSCALE_OFFSET].reshape(TOKENS, DIM // NV_BLOCK)[off]
+        sb[r] = pages[page, NVFP4_TSCALE_OFFSET:].reshape(TOKENS, 4)[off]
+    codes = np.empty((t.size, DIM), dtype=np.uint8)
+    codes[:, 0::2] = packed & 0xF
+    codes[:, 1::2] = packed >> 4
+    return nvfp4_dequantize(codes, cb, sb.view("<f4").reshape(t.size))
+
+
+PAGE_BYTES = {"mxfp4": MXFP4_PAGE_BYTES, "fp8": FP8_PAGE_BYTES, "nvfp4": NVFP4_PAGE_BYTES}
+STORE = {"mxfp4": mxfp4_store, "fp8": fp8_store, "nvfp4": nvfp4_store}
+READ = {"mxfp4": mxfp4_read, "fp8": fp8_read, "nvfp4": nvfp4_read}

@@ -41,7 +41,9 @@ def attention_query(inp) -> tuple:
     """(query as float64 [B][q][H][128], e4m3 codes or None).
 
     MXFP4 main KV: the query is stored as saturating e4m3 with unit scale and the
-    split stage consumes those codes. FP8 main KV: the bf16 query is used as is."""
+    split stage consumes those codes. FP8 and NVFP4 main KV: the bf16 query is
+    used as is (the e4m3 query store is the MXFP4 path's; a reading for NVFP4,
+    which the pages do not describe)."""
     wl = inp.wl
     if wl.kv_format == "mxfp4":
         src = formats.bf16_to_f64(inp.q_bf16) if wl.q_dtype == "bf16" else inp.q.astype(np.float64)

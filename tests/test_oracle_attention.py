@@ -107,13 +107,16 @@ def _tiny(**kw):
     return W.make_inputs(W.WORKLOADS["tiny"].with_(**kw))
 
 
-def test_step_dense_topk_equals_sdpa_over_dequantized_cache():
-    inp = _tiny(topk=16)                        # 16 pages: top-k covers every block
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_step_dense_topk_equals_sdpa_over_dequantized_cache(fmt):
+    inp = _tiny(topk=16, kv_format=fmt, idx_format=fmt)    # 16 pages: top-k covers every block
     r = S.decode_step_ref(inp)
     assert list(r["block_table"][0, 0]) == list(range(16))
     L = int(inp.contexts[0])
-    K = F.mxfp4_read(r["pools"]["k"], inp.page_table[0], L)
-    V = F.mxfp4_read(r["pools"]["v"], inp.page_table[0], L)
+    K = F.READ[fmt](r["pools"]["k"], inp.page_table[0], L)
+    V = F.READ[fmt](r["pools"]["v"], inp.page_table[0], L)
+    # the cache holds the quantized rows: within the format's error of the fp32 rows
+    assert np.abs(K - inp.rows("k", 0)).max() <= 0.25 * np.abs(inp.rows("k", 0)).max()
     qa, codes = S.attention_query(inp)
     ref = torch.nn.functional.scaled_dot_product_attention(
         torch.from_numpy(qa[0, 0])[None, :, None], torch.from_numpy(K)[None, None].expand(1, 4, L, 128),
@@ -145,12 +148,13 @@ def test_step_page_table_permutation_invariance():
     np.testing.assert_array_equal(r["O"], r2["O"])
 
 
-def test_step_poison_vs_zero_tails_identical():
-    wl = W.WORKLOADS["tiny"].with_(ctx_rule=("fixed", 2000))     # last page partly filled
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_step_poison_vs_zero_tails_identical(fmt):
+    wl = W.WORKLOADS["tiny"].with_(ctx_rule=("fixed", 2000), kv_format=fmt, idx_format=fmt)   # last page partly filled
     inp = W.make_inputs(wl)
-    pre = {s: S.build_cache(inp, s, "mxfp4") for s in ("k", "v", "idx")}
+    pre = {s: S.build_cache(inp, s, fmt) for s in ("k", "v", "idx")}
     r = S.decode_step_ref(inp, pools=pre)
-    zero = {s: S.build_cache(inp, s, "mxfp4", fill=0) for s in ("k", "v", "idx")}
+    zero = {s: S.build_cache(inp, s, fmt, fill=0) for s in ("k", "v", "idx")}
     r2 = S.decode_step_ref(inp, pools=zero)
     np.testing.assert_array_equal(r["O"], r2["O"])
     np.testing.assert_array_equal(r["block_table"], r2["block_table"])

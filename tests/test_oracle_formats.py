@@ -22,6 +22,8 @@ def test_page_sizes_closed_form():
     assert F.MXFP4_PAGE_BYTES == 128 * 128 // 2 + 128 * 128 // 32 == 8704
     # 128 x 128 e4m3 bytes + one fp32 scale per token
     assert F.FP8_PAGE_BYTES == 128 * 128 + 128 * 4 == 16896
+    # 128 x 128 x 4 bits + one e4m3 byte per 16 elements + one fp32 scale per token
+    assert F.NVFP4_PAGE_BYTES == 128 * 128 // 2 + 128 * 128 // 16 + 128 * 4 == 9728
 
 
 # ---------------------------------------------------------------- e2m1
@@ -192,7 +194,7 @@ def test_fp8_rows_roundtrip_bound():
 
 
 # ---------------------------------------------------------------- pages
-@pytest.mark.parametrize("fmt", ["mxfp4", "fp8"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "fp8", "nvfp4"])
 def test_store_read_and_poison(fmt):
     rng = np.random.default_rng(2)
     L = 300                                            # 3 pages, last one partly filled
@@ -204,6 +206,8 @@ def test_store_read_and_poison(fmt):
     got = F.READ[fmt](pool, table, L)
     if fmt == "mxfp4":
         want = F.mxfp4_dequantize(*F.mxfp4_quantize_rows(x))
+    elif fmt == "nvfp4":
+        want = F.nvfp4_dequantize(*F.nvfp4_quantize_rows(x))
     else:
         c, s = F.fp8_quantize_rows(x)
         want = F.E4M3_TABLE[c.astype(np.int64)] * s[:, None].astype(np.float64)
@@ -280,3 +284,148 @@ def test_page_table_permutation_invariance():
     a = F.mxfp4_read(pool, table, L)
     b = F.mxfp4_read(pool2.reshape(-1), perm[table].astype(np.int32), L)
     np.testing.assert_array_equal(a, b)
+
+
+# ---------------------------------------------------------------- NVFP4 (reading)
+# e2m1 elements in 16-element blocks with e4m3 block scales and a per-token fp32
+# scale S = amax / 2688; c_b = e4m3(a_b / 6 S); code = e2m1(x / (e4m3(c_b) S)).
+# Every expected byte below is worked out by hand from those rules.
+def _nv_worked_row():
+    x = np.zeros(128, dtype=np.float32)
+    x[0], x[1], x[2] = 2688.0, -1344.0, 224.0     # block 0: a = 2688 -> 448 = 0x7E; 6, -3, 0.5 -> 7, 0xD, 1
+    x[16], x[17], x[18] = 1.0, 1.5, -0.75         # block 1: a = 1.5 -> 0.25 = 0x28; 4, 6, -3 -> 6, 7, 0xD
+    x[32], x[33], x[34], x[35] = 3.0, 0.125, 0.375, -1.25   # block 2: 0.5 = 0x30; 6, .25, .75, -2.5 -> 7, 0, 2, 0xC
+    # block 3 (elements 48..63) all zero: scale code 0, codes 0
+    x[64], x[65] = 6.375, -6.375                  # block 4: 6.375 / 6 = 1.0625, a tie -> 1.0 = 0x38; 6.375 saturates to 6
+    x[80] = 1e-6                                  # block 5: 1e-6 / 6 below half of 2^-9 -> scale code 0, codes 0
+    x[96], x[97] = 6 * 2.0 ** -8, 2.0 ** -9       # block 6: 2^-8 = subnormal 2 * 2^-9 -> 0x02; 6, 0.5 -> 7, 1
+    x[112], x[113] = -96.0, 40.0                  # block 7: 16 = 2^4 -> 0x58; -6, 2.5 -> 0xF, 4
+    codes = np.zeros(64, dtype=np.uint8)
+    codes[0], codes[1] = 0xD7, 0x01
+    codes[8], codes[9] = 0x76, 0x0D
+    codes[16], codes[17] = 0x07, 0xC2
+    codes[32] = 0xF7
+    codes[48] = 0x17
+    codes[56] = 0x4F
+    return x, codes, [0x7E, 0x28, 0x30, 0x00, 0x38, 0x00, 0x02, 0x58]
+
+
+def test_nvfp4_worked_bytes():
+    """One page, three tokens: a zero row, the worked row (S = 1) and the worked
+    row times 2^-20 (S = 2^-20 exactly, every quotient unchanged): codes at
+    64 t, block scales at 8192 + 8 t, token scale at 9216 + 4 t."""
+    x, codes, cb = _nv_worked_row()
+    rows = np.stack([np.zeros(128, dtype=np.float32), x, x * np.float32(2.0 ** -20)])
+    pool = W.new_pool(1, F.NVFP4_PAGE_BYTES)
+    F.nvfp4_store(pool, np.array([0], dtype=np.int32), 1, rows)       # positions 1, 2, 3
+    assert (pool[64:128] == 0).all() and (pool[8192 + 8:8192 + 16] == 0).all()
+    assert list(pool[9216 + 4:9216 + 8]) == [0x00, 0x00, 0x80, 0x3F]            # 1.0f for the zero row
+    for t, s_bytes in ((2, [0x00, 0x00, 0x80, 0x3F]), (3, [0x00, 0x00, 0x80, 0x35])):   # 1.0f, 2^-20
+        np.testing.assert_array_equal(pool[64 * t:64 * t + 64], codes)
+        assert list(pool[8192 + 8 * t:8192 + 8 * t + 8]) == cb
+        assert list(pool[9216 + 4 * t:9216 + 4 * t + 4]) == s_bytes
+    # untouched bytes stay poisoned
+    assert (pool[:64] == 0xFF).all() and (pool[256:8192] == 0xFF).all()
+    assert (pool[8192:8200] == 0xFF).all() and (pool[8224:9216] == 0xFF).all()
+    assert (pool[9216:9220] == 0xFF).all() and (pool[9232:] == 0xFF).all()
+    # the read path: e2m1 * e4m3 * S
+    got = F.nvfp4_read(pool, np.array([0], dtype=np.int32), 4, np.array([2, 3]))
+    want = np.zeros(128)
+    want[[0, 1, 2]] = [2688.0, -1344.0, 224.0]
+    want[[16, 17, 18]] = [1.0, 1.5, -0.75]
+    want[[32, 33, 34, 35]] = [3.0, 0.0, 0.5, -1.0]           # 0.125 -> 0, 0.375 -> 1 * 0.5, -1.25 -> -2 * 0.5
+    want[[64, 65]] = [6.0, -6.0]
+    want[[96, 97]] = [6 * 2.0 ** -8, 2.0 ** -9]
+    want[[112, 113]] = [-96.0, 32.0]
+    np.testing.assert_array_equal(got[0], want)
+    np.testing.assert_array_equal(got[1], want * 2.0 ** -20)
+
+
+def _nv_brute(x):
+    """The NVFP4 reading by exhaustive nearest-value search over every e4m3 and
+    e2m1 code (ties to the even code, saturation at the largest value)."""
+    x = np.asarray(x, dtype=np.float32)
+    e4 = F.E4M3_TABLE[:127]
+    e2 = F.E2M1_TABLE[:8]
+
+    def nearest(table, v):
+        v = min(v, table[-1])
+        d = np.abs(table - v)
+        best = np.flatnonzero(d == d.min())
+        return int(best[0]) if len(best) == 1 else int(best[best % 2 == 0][0])
+
+    amax = np.float32(np.abs(x).max())
+    S = np.float32(1.0) if amax == 0 else max(np.float32(amax / np.float32(2688.0)), np.float32(2.0 ** -149))
+    codes = np.zeros(128, dtype=np.uint8)
+    cb = np.zeros(8, dtype=np.uint8)
+    for b in range(8):
+        blk = x[16 * b:16 * b + 16]
+        t = np.float32(np.float32(np.abs(blk).max()) / np.float32(np.float32(6.0) * S))
+        cb[b] = nearest(e4, float(t))
+        d = np.float32(np.float32(e4[cb[b]]) * S)
+        for i, v in enumerate(blk):
+            if d > 0:
+                q = np.float32(v / d)
+                codes[16 * b + i] = nearest(e2, abs(float(q))) | (8 if np.signbit(q) else 0)
+    return codes, cb, S
+
+
+def test_nvfp4_brute_force():
+    rng = np.random.default_rng(13)
+    rows = [rng.standard_normal(128) * 10.0 ** rng.uniform(-30, 30) for _ in range(40)]
+    r = rng.standard_normal(128)
+    r[rng.integers(0, 128, 4)] *= 20.0                      # outliers
+    rows.append(r)
+    r = rng.standard_normal(128)
+    r[16:32] = 0.0                                           # a zero block
+    r[48:64] *= 1e-7                                         # a block far below the row's scale
+    rows.append(r)
+    rows.append(np.full(128, -3.0))                          # a constant row
+    with np.errstate(under="ignore"):
+        rows.append(rng.standard_normal(128) * 1e-41)            # subnormal fp32: S clamps at 2^-149
+    x = np.stack(rows).astype(np.float32)
+    codes, cb, S = F.nvfp4_quantize_rows(x)
+    for n in range(x.shape[0]):
+        bc, bcb, bS = _nv_brute(x[n])
+        assert S[n] == bS, n
+        np.testing.assert_array_equal(cb[n], bcb, err_msg=f"row {n}")
+        np.testing.assert_array_equal(codes[n], bc, err_msg=f"row {n}")
+
+
+def test_nvfp4_roundtrip_on_grid():
+    """Rows built from representable values (each block holding +-6 times its
+    scale, token scale a power of two) come back exactly."""
+    rng = np.random.default_rng(17)
+    N = 200
+    c = rng.integers(0, 16, (N, 8, 16))
+    c[:, :, 0] = 7 | (rng.integers(0, 2, (N, 8)) << 3)      # +-6 in every block
+    cb = rng.integers(1, 127, (N, 8))                        # any finite non-zero e4m3
+    cb[:, 0] = 0x7E                                          # block 0 holds the row's amax (6 * 448)
+    S = 2.0 ** rng.integers(-40, 40, N)
+    x = (F.E2M1_TABLE[c] * F.E4M3_TABLE[cb][:, :, None] * S[:, None, None]).reshape(N, 128).astype(np.float32)
+    with np.errstate(under="ignore"):
+        codes, gcb, gS = F.nvfp4_quantize_rows(x)
+    np.testing.assert_array_equal(gS, S.astype(np.float32))
+    np.testing.assert_array_equal(gcb, cb)
+    np.testing.assert_array_equal(F.nvfp4_dequantize(codes, gcb, gS), x.astype(np.float64))
+
+
+@settings(max_examples=40, deadline=None)
+@given(st.integers(0, 2**31 - 1))
+def test_nvfp4_error_bound(seed):
+    """|x - x^| <= (9/8) a_b / 6 + 2^-10 * 6 S per block: the e2m1 step is at
+    most 2 (half-step 1) in units of d_b ~ a_b / 6, the e4m3 rounding of the
+    block scale (3 mantissa bits) moves d_b by at most 1/16 relative, and a
+    block whose scale rounds below e4m3's range is stored as zeros."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((64, 128)) * 10.0 ** rng.uniform(-6, 6, (64, 1))).astype(np.float32)
+    x[rng.random((64, 128)) < 0.01] *= 20.0
+    codes, cb, S = F.nvfp4_quantize_rows(x)
+    dq = F.nvfp4_dequantize(codes, cb, S).reshape(64, 8, 16)
+    ab = np.abs(x).reshape(64, 8, 16).max(axis=2).astype(np.float64)
+    bound = 1.125 * ab / 6.0 + 2.0 ** -10 * 6.0 * S[:, None].astype(np.float64)
+    err = np.abs(dq - x.reshape(64, 8, 16)).max(axis=2)
+    assert (err <= bound * (1 + 1e-6)).all()
+    # the element holding the row's amax decodes to +-6 * 448 * S
+    i = np.abs(x).argmax(axis=1)
+    np.testing.assert_array_equal(np.abs(dq.reshape(64, 128)[np.arange(64), i]), 2688.0 * S.astype(np.float64))

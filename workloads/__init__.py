@@ -20,15 +20,19 @@ Workloads (the shapes of the pages' decode configurations, one TP rank's share):
 - ``long``   B=4, q=8, MXFP4, ragged contexts U[131072, 262144], top-k 32.
 - ``headline`` B=4, q=8, MXFP4, every context 262144, top-k 32, full step.
 - ``b32``    B=32, q=8, MXFP4, ragged U[8192, 262144], top-k 32, full step.
+- ``nvfp4``  B=4, q=8, 16:1, NVFP4 K/V and index (e2m1 in 16-element blocks,
+             e4m3 block scales, per-token fp32 scale), context 16384 - u,
+             top-k 16, 1 % outliers x20.
 
 Values: K, V, index-K and q are N(0, 1) fp32; with ``outliers`` about 1 % of
 the elements (Binomial(N, 0.01) uniformly drawn positions) are multiplied by 20. Index queries are bf16 (fp32 N(0,1)
 rounded to nearest even); index-head weights are U(0, 1) fp32.
 
-Pools: every cache pool starts filled with the byte 0xFF. In both cache formats
-that byte pattern decodes to NaN (an all-ones e8m0 scale, an e4m3 0xFF code, an
-all-ones fp32 scale), so unused pages and the unwritten tail of a partly filled
-page are NaN-poisoned without this module knowing the page layout.
+Pools: every cache pool starts filled with the byte 0xFF. In every cache format
+that byte pattern decodes to NaN (an all-ones e8m0 scale, an e4m3 0xFF code or
+block scale, an all-ones fp32 scale), so unused pages and the unwritten tail of
+a partly filled page are NaN-poisoned without this module knowing the page
+layout.
 """
 from __future__ import annotations
 
@@ -55,8 +59,8 @@ class Workload:
     H: int                 # query heads sharing the one KV head
     H_I: int               # index heads
     topk: int
-    kv_format: str         # "mxfp4" | "fp8"
-    idx_format: str        # "mxfp4" | "fp8"
+    kv_format: str         # "mxfp4" | "fp8" | "nvfp4"
+    idx_format: str        # "mxfp4" | "fp8" | "nvfp4"
     q_dtype: str           # dtype of the attention q handed to the step: "f32" | "bf16"
     outliers: bool
     ctx_rule: tuple        # ("fixed", L) | ("fixed_minus_u", L, umax) | ("uniform", lo, hi) | ("list", (...))
@@ -102,6 +106,8 @@ WORKLOADS = {
                          ("fixed", 262144)),
     "b32": Workload("b32", 4, 32, 8, 16, 4, 32, "mxfp4", "mxfp4", "f32", True,
                     ("uniform", 8192, 262144)),
+    "nvfp4": Workload("nvfp4", 6, 4, 8, 16, 4, 16, "nvfp4", "nvfp4", "bf16", True,
+                      ("fixed_minus_u", 16384, 127)),
 }
 
 
