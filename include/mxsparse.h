@@ -1,6 +1,6 @@
 /*
  * mxsparse — one tensor-parallel rank's sparse-attention decode step over
- * MXFP4 (or FP8) paged caches, for AMD MI355X (gfx950).
+ * MXFP4 (or FP8, or NVFP4) paged caches, for AMD MI355X (gfx950).
  *
  * The step (ATOM PR #2812, "[MiniMax-M3.1] Mono decode over the MXFP4 KV and
  * index caches": What, and its commit messages):
@@ -42,6 +42,14 @@
  *     96-127) at bytes 8192 + 4 t + g.
  *   FP8 page, 16896 B: token t has its 128 e4m3 codes at [128 t, 128 t + 128)
  *     and its fp32 scale at 16384 + 4 t (value = e4m3(code) * scale).
+ *   NVFP4 page, 9728 B: token t has its codes at [64 t, 64 t + 64) as in the
+ *     MXFP4 page, the e4m3 scale codes of its eight 16-element blocks at
+ *     8192 + 8 t + b and its fp32 scale at 9216 + 4 t (value = e2m1(code) *
+ *     e4m3(block code) * scale). The pages name NVFP4 K/V and index caches
+ *     (ATOM PR #2686, timeline entry #2744; ATOM PR #2812, commit messages)
+ *     without defining them: this is the public NVFP4 layout (e2m1 in
+ *     16-element blocks, e4m3 block scales, a second-level fp32 scale) with the
+ *     second level kept per token, a reading.
  * Slot s of a pool is token s % 128 of page s / 128.
  *
  * Shapes: head_dim 128 everywhere; one KV head shared by H query heads (GQA);
@@ -69,19 +77,20 @@ typedef enum {
     MXS_ELAUNCH = 4          /* the HIP runtime rejected a launch                     */
 } mxs_status;
 
-typedef enum { MXS_FMT_MXFP4 = 0, MXS_FMT_FP8 = 1 } mxs_format;
+typedef enum { MXS_FMT_MXFP4 = 0, MXS_FMT_FP8 = 1, MXS_FMT_NVFP4 = 2 } mxs_format;
 typedef enum { MXS_F32 = 0, MXS_BF16 = 1, MXS_E4M3 = 2 } mxs_dtype;
 
 #define MXS_PAGE_TOKENS 128
 #define MXS_HEAD_DIM 128
 #define MXS_MXFP4_PAGE_BYTES 8704
 #define MXS_FP8_PAGE_BYTES 16896
+#define MXS_NVFP4_PAGE_BYTES 9728
 
 /* Refusal limits (MXS_EUNSUPPORTED): H <= 16 query heads per KV head,
  * 1 <= H_I <= 4 index heads, q <= 16 query rows per sequence, topk <= 64,
  * page_table_stride <= 8192 pages (1M tokens), partitions <= 64.
- * Formats other than MXFP4 and FP8 (e.g. NVFP4) are refused: the pages name
- * them as refused by the Mono dispatch (same PR, commit messages). */
+ * Format ids other than MXS_FMT_MXFP4, MXS_FMT_FP8 and MXS_FMT_NVFP4 are
+ * refused. */
 #define MXS_MAX_H 16
 #define MXS_MAX_H_I 4
 #define MXS_MAX_Q 16
@@ -120,11 +129,19 @@ typedef struct {
  * (1 for an all-zero row), codes = saturating e4m3 of fp32(x / scale). The
  * pages give an FP8 cache with a per-token fp32 scale but no rule (ATOM PR
  * #2686, "Enable Mono decode with fixed DSpark verify", Summary); this rule is
- * a reading. */
+ * a reading.
+ * nvfp4_row_store: the same for an NVFP4 pool [num_pages][9728] (a reading, see
+ * the page layouts above): per token S = fp32(amax / 2688) (2688 = 6 * 448; 1
+ * for an all-zero row, 2^-149 where the quotient underflows to 0); per
+ * 16-element block c_b = saturating e4m3 of fp32(a_b / fp32(6 S)), a_b the
+ * block's largest magnitude; each element e2m1 of fp32(x / fp32(e4m3(c_b) S)),
+ * code 0 where that divisor is 0. */
 int mxfp4_row_store(const float *rows, int64_t n, const int64_t *slots, uint8_t *pages,
                     int32_t num_pages, void *stream);
 int fp8_row_store(const float *rows, int64_t n, const int64_t *slots, uint8_t *pages,
                   int32_t num_pages, void *stream);
+int nvfp4_row_store(const float *rows, int64_t n, const int64_t *slots, uint8_t *pages,
+                    int32_t num_pages, void *stream);
 
 /* ---- 2. q store ----------------------------------------------------------
  * pack_q_e4m3: n elements of q (fp32 or bf16 per q_dtype) to OCP e4m3 codes
@@ -174,7 +191,7 @@ size_t mxs_score_workspace_bytes(int32_t B, int32_t q, int32_t page_table_stride
  * A partition without tokens writes (m, l, o) = (-inf, 0, 0) (same PR, commit
  * message of the MXFP4 main-KV commit: split stage, sp_o / sp_m / sp_l).
  *   q     MXFP4 KV: e4m3 codes (q_dtype MXS_E4M3) [B][q][H][128];
- *         FP8 KV: bf16 bits (q_dtype MXS_BF16) [B][q][H][128]; 16 B aligned
+ *         FP8 or NVFP4 KV: bf16 bits (q_dtype MXS_BF16) [B][q][H][128]; 16 B aligned
  *   block_table [B][q][topk] int32 block ids (-1 = empty slot)
  *   sp_m, sp_l  [B][q][H][P] fp32;  sp_o [B][q][H][P][128] fp32 (outputs)
  * P = num_partitions in 1..64 (0: mxs_default_partitions). */
@@ -204,7 +221,8 @@ typedef struct {
     const float *v_new;        /*   the cache already holds them (no row store)           */
     const float *idx_new;
     const void *query;         /* attention query [B][q][H][128]: MXFP4 KV takes fp32 or
-                                  bf16 (q_dtype) and stores it as e4m3; FP8 KV takes bf16 */
+                                  bf16 (q_dtype) and stores it as e4m3; FP8 and NVFP4
+                                  KV take bf16                                          */
     int32_t q_dtype;
     const uint16_t *q_idx;     /* [B][q][H_I][128] bf16 bits                            */
     const float *w;            /* [B][q][H_I] fp32                                      */

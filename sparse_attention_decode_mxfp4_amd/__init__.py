@@ -17,12 +17,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmxsparse.so")
 
 MXS_OK, MXS_EINVAL, MXS_EUNSUPPORTED, MXS_EWORKSPACE, MXS_ELAUNCH = range(5)
-FMT = {"mxfp4": 0, "fp8": 1}
+FMT = {"mxfp4": 0, "fp8": 1, "nvfp4": 2}
 MXS_F32, MXS_BF16, MXS_E4M3 = 0, 1, 2
-PAGE_BYTES = {"mxfp4": 8704, "fp8": 16896}
+PAGE_BYTES = {"mxfp4": 8704, "fp8": 16896, "nvfp4": 9728}
 
 EXPORTS = [
-    "mxfp4_row_store", "fp8_row_store", "pack_q_e4m3", "index_score", "topk_blocks",
+    "mxfp4_row_store", "fp8_row_store", "nvfp4_row_store", "pack_q_e4m3", "index_score", "topk_blocks",
     "index_score_topk", "mxs_score_workspace_bytes", "sparse_split_attn", "mxs_default_partitions",
     "lse_merge", "decode_step", "decode_step_reuse", "mxs_workspace_bytes", "mxs_status_str", "mxs_last_error",
     "mxs_abi_version", "mxs_read_index_pages", "decode_step_noalloc", "mxs_workspace_init",
@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
         sig = {
             "mxfp4_row_store": [P, I64, P, P, I32, P],
             "fp8_row_store": [P, I64, P, P, I32, P],
+            "nvfp4_row_store": [P, I64, P, P, I32, P],
             "pack_q_e4m3": [P, I32, I64, P, P],
             "index_score": [P, P, P, I32, I32, I32, P, P],
             "topk_blocks": [P, P, I32, I32, I32, P, P],
@@ -180,6 +181,13 @@ def fp8_row_store(rows, slots, pages):
     _check(lib().fp8_row_store(_dev(rows, torch.float32, "rows", (n, 128)), n,
                                _dev(slots, torch.int64, "slots", (n,)), _dev(pages, torch.uint8, "pages"),
                                pages.numel() // PAGE_BYTES["fp8"], _stream()))
+
+
+def nvfp4_row_store(rows, slots, pages):
+    n = rows.shape[0]
+    _check(lib().nvfp4_row_store(_dev(rows, torch.float32, "rows", (n, 128)), n,
+                                 _dev(slots, torch.int64, "slots", (n,)), _dev(pages, torch.uint8, "pages"),
+                                 pages.numel() // PAGE_BYTES["nvfp4"], _stream()))
 
 
 def pack_q_e4m3(q, q8=None):

@@ -49,11 +49,13 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
     if (!(cond)) return fail(code, __VA_ARGS__); \
   } while (0)
 
-size_t page_bytes(int fmt) { return fmt == MXS_FMT_MXFP4 ? MXS_MXFP4_PAGE_BYTES : MXS_FP8_PAGE_BYTES; }
+size_t page_bytes(int fmt) {
+  return fmt == MXS_FMT_MXFP4 ? MXS_MXFP4_PAGE_BYTES : (fmt == MXS_FMT_FP8 ? MXS_FP8_PAGE_BYTES : MXS_NVFP4_PAGE_BYTES);
+}
 
 int check_format(int fmt, const char *name) {
-  REQ(fmt == MXS_FMT_MXFP4 || fmt == MXS_FMT_FP8, MXS_EUNSUPPORTED,
-      "%s: format %d is not supported (MXFP4 = 0 and FP8 = 1 are; NVFP4 is refused)", name, fmt);
+  REQ(fmt == MXS_FMT_MXFP4 || fmt == MXS_FMT_FP8 || fmt == MXS_FMT_NVFP4, MXS_EUNSUPPORTED,
+      "%s: format %d is not supported (MXFP4 = 0, FP8 = 1 and NVFP4 = 2 are)", name, fmt);
   return MXS_OK;
 }
 
@@ -175,6 +177,11 @@ int fp8_row_store(const float *rows, int64_t n, const int64_t *slots, uint8_t *p
   return row_store(MXS_FMT_FP8, rows, n, slots, pages, num_pages, stream, "fp8_row_store");
 }
 
+int nvfp4_row_store(const float *rows, int64_t n, const int64_t *slots, uint8_t *pages, int32_t num_pages,
+                    void *stream) {
+  return row_store(MXS_FMT_NVFP4, rows, n, slots, pages, num_pages, stream, "nvfp4_row_store");
+}
+
 int pack_q_e4m3(const void *q, int32_t q_dtype, int64_t n, uint8_t *q8, void *stream) {
   REQ(q_dtype == MXS_F32 || q_dtype == MXS_BF16, MXS_EUNSUPPORTED, "pack_q_e4m3: q_dtype %d (fp32 or bf16 only)",
       q_dtype);
@@ -266,7 +273,7 @@ static int check_attn_args(const mxs_cache *cache, const void *q, int32_t q_dtyp
   if (cache->kv_format == MXS_FMT_MXFP4)
     REQ(q_dtype == MXS_E4M3, MXS_EUNSUPPORTED, "q_dtype: %d; an MXFP4 KV cache takes an e4m3 query", q_dtype);
   else
-    REQ(q_dtype == MXS_BF16, MXS_EUNSUPPORTED, "q_dtype: %d; an FP8 KV cache takes a bf16 query", q_dtype);
+    REQ(q_dtype == MXS_BF16, MXS_EUNSUPPORTED, "q_dtype: %d; an FP8 or NVFP4 KV cache takes a bf16 query", q_dtype);
   REQ(q && aligned(q, 16), MXS_EINVAL, "q: null or not 16-byte aligned");
   REQ(block_table && aligned(block_table, 4), MXS_EINVAL, "block_table: null or misaligned");
   return MXS_OK;
@@ -340,7 +347,8 @@ static int step_entry(const mxs_step *a, void *ws, size_t ws_bytes, void *stream
     REQ(a->q_dtype == MXS_F32 || a->q_dtype == MXS_BF16, MXS_EUNSUPPORTED,
         "q_dtype: %d; an MXFP4 KV step takes an fp32 or bf16 query and stores it as e4m3", a->q_dtype);
   else
-    REQ(a->q_dtype == MXS_BF16, MXS_EUNSUPPORTED, "q_dtype: %d; an FP8 KV step takes a bf16 query", a->q_dtype);
+    REQ(a->q_dtype == MXS_BF16, MXS_EUNSUPPORTED, "q_dtype: %d; an FP8 or NVFP4 KV step takes a bf16 query",
+        a->q_dtype);
   REQ(a->query && aligned(a->query, 16), MXS_EINVAL, "query: null or not 16-byte aligned");
   const bool store = a->k_new || a->v_new || a->idx_new;
   if (store)
@@ -451,7 +459,8 @@ int decode_step_reuse(const mxs_step *a, const int32_t *block_table, void *ws, s
     REQ(a->q_dtype == MXS_F32 || a->q_dtype == MXS_BF16, MXS_EUNSUPPORTED,
         "q_dtype: %d; an MXFP4 KV step takes an fp32 or bf16 query and stores it as e4m3", a->q_dtype);
   else
-    REQ(a->q_dtype == MXS_BF16, MXS_EUNSUPPORTED, "q_dtype: %d; an FP8 KV step takes a bf16 query", a->q_dtype);
+    REQ(a->q_dtype == MXS_BF16, MXS_EUNSUPPORTED, "q_dtype: %d; an FP8 or NVFP4 KV step takes a bf16 query",
+        a->q_dtype);
   REQ(a->query && aligned(a->query, 16), MXS_EINVAL, "query: null or not 16-byte aligned");
   REQ(!a->k_new == !a->v_new, MXS_EINVAL, "k_new / v_new: give both or neither");
   REQ((!a->k_new || aligned(a->k_new, 8)) && (!a->v_new || aligned(a->v_new, 8)), MXS_EINVAL,

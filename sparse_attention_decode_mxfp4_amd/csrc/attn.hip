@@ -39,6 +39,9 @@
 // * FP8 KV (e4m3 codes, per-token fp32 scale, bf16 query): QK on the bf16
 //   MFMA with the codes widened exactly to bf16 and the token scale applied to
 //   the dot product; PV folds the token scale into P.
+// * NVFP4 KV (e2m1 in 16-element blocks with e4m3 block scales, per-token fp32
+//   scale, bf16 query): the MXFP4 lane layout, the codes widened to bf16 times
+//   their block scale (exact), the token scale handled as for FP8.
 #include "common.hpp"
 #include "launch.hpp"
 #include "topk.hpp"
@@ -59,11 +62,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 // the high halves, x's in the low half of the result.
 __device__ __forceinline__ uint32_t lo_pair(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x05040100u); }
 __device__ __forceinline__ uint32_t hi_pair(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x07060302u); }
-// Two fp32 as a bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
-  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
 // fp32 value of an e8m0 scale byte for the cvt_scalef32 instructions:
 // byte << 23 is 2^(byte - 127) for byte >= 1, and byte 0 takes 0x400000 = 2^-127.
 __device__ __forceinline__ float e8m0_scale(uint32_t byte) { return u2f(max(byte << 23, 0x00400000u)); }
@@ -77,9 +75,16 @@ __device__ __forceinline__ float e8m0_scale(uint32_t byte) { return u2f(max(byte
 //  V: k-step s -> the 8 tokens toff + te(s, e); MXFP4: 4 bytes (codes 8 n ..
 //     8 n + 7) per token + the scale dwords of the two 4-token runs; FP8: 8
 //     bytes per token + the fp32 scales of the two runs.
+//  NVFP4: K as MXFP4 with the two block scale codes of group kg (kb) and the
+//     fp32 scales of tokens toff + 16 nt + 4 kg + i (ks, as FP8); V as MXFP4
+//     with, per token, the dword holding the scale code of block n / 2 (vb)
+//     and the fp32 scales of the two runs (vs, as FP8).
 template <int FMT, int NT> struct BlockRegs;
 template <int NT> struct BlockRegs<0, NT> { u32x4 k[NT]; uint32_t ks[NT]; uint32_t v[NT / 2][8]; u32x4 vs[NT / 2][2]; };
 template <int NT> struct BlockRegs<1, NT> { u32x4 k[NT][2]; f32x4 ks[NT]; uint2 v[NT / 2][8]; f32x4 vs[NT / 2][2]; };
+template <int NT> struct BlockRegs<2, NT> {
+  u32x4 k[NT]; uint32_t kb[NT]; f32x4 ks[NT]; uint32_t v[NT / 2][8]; uint32_t vb[NT / 2][8]; f32x4 vs[NT / 2][2];
+};
 
 // token of element e of the lane's k-group in PV k-step s
 __device__ __forceinline__ int pv_token(int s, int kg, int e) { return 32 * s + (e < 4 ? 4 * kg + e : 16 + 4 * kg + e - 4); }
@@ -102,6 +107,30 @@ __device__ __forceinline__ void load_block(BlockRegs<FMT, NT> &r, const uint8_t 
       r.vs[s][0] = *reinterpret_cast<const u32x4 *>(vp + kMxScaleOff + 4 * (toff + pv_token(s, kg, 0)));
       r.vs[s][1] = *reinterpret_cast<const u32x4 *>(vp + kMxScaleOff + 4 * (toff + pv_token(s, kg, 4)));
     }
+  } else if constexpr (FMT == 2) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int tok = toff + 16 * nt + n;
+      r.k[nt] = *reinterpret_cast<const u32x4 *>(kp + 64 * tok + 16 * kg);
+      r.kb[nt] = *reinterpret_cast<const uint16_t *>(kp + kNvBScaleOff + 8 * tok + 2 * kg);
+      r.ks[nt] = *reinterpret_cast<const f32x4 *>(kp + kNvTScaleOff + 4 * (toff + 16 * nt + 4 * kg));
+    }
+    // one lane base each for the codes and the block scale dwords, constant
+    // offsets from there (computed per load, the block scale addresses took
+    // enough registers to spill)
+    const uint8_t *vcode = vp + 64 * (toff + 4 * kg) + 4 * n;
+    const uint8_t *vbsc = vp + kNvBScaleOff + 8 * (toff + 4 * kg) + 4 * (n >> 3);
+#pragma unroll
+    for (int s = 0; s < NT / 2; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int dt = pv_token(s, 0, e);              // the token's offset from toff + 4 kg
+        r.v[s][e] = *reinterpret_cast<const uint32_t *>(vcode + 64 * dt);
+        r.vb[s][e] = *reinterpret_cast<const uint32_t *>(vbsc + 8 * dt);
+      }
+      r.vs[s][0] = *reinterpret_cast<const f32x4 *>(vp + kNvTScaleOff + 4 * (toff + pv_token(s, kg, 0)));
+      r.vs[s][1] = *reinterpret_cast<const f32x4 *>(vp + kNvTScaleOff + 4 * (toff + pv_token(s, kg, 4)));
+    }
   } else {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -123,11 +152,10 @@ __device__ __forceinline__ void load_block(BlockRegs<FMT, NT> &r, const uint8_t 
 
 // The lane's query elements for QK, as loaded: head n, elements 32 kg + 8 s
 // .. + 7 for k-step s (the order of the key groups each lane loads); e4m3
-// codes with an MXFP4 cache, bf16 with an FP8 cache. Heads >= H load head 0
-// (unconditional loads) and are zeroed when the operands are formed.
-template <int FMT> struct QueryRegs;
+// codes with an MXFP4 cache, bf16 with an FP8 or NVFP4 cache. Heads >= H load
+// head 0 (unconditional loads) and are zeroed when the operands are formed.
+template <int FMT> struct QueryRegs { u32x4 c[4]; };
 template <> struct QueryRegs<0> { uint2 c[4]; };
-template <> struct QueryRegs<1> { u32x4 c[4]; };
 
 template <int FMT, bool COH = false>
 __device__ __forceinline__ void load_query(const void *__restrict__ qv, int row, int H, int n, int kg,
@@ -179,7 +207,7 @@ __device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t
                                              const QueryRegs<FMT> &q, int H, float qk_scale2, float &m_run,
                                              float &l_run, f32x4 O[8], int n, int kg) {
   const float NEG_INF = -__builtin_inff();
-  const int64_t pb = (int64_t)phys * (FMT == 0 ? kMxPageBytes : kF8PageBytes);
+  const int64_t pb = (int64_t)phys * kPageBytes<FMT>;
   BlockRegs<FMT, NT> r;
   load_block<FMT, NT>(r, c.k_pages + pb, c.v_pages + pb, toff, n, kg);
   // The query is widened here, after the pages are requested: the empty asm
@@ -197,12 +225,18 @@ __device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t
   for (int nt = 0; nt < NT; ++nt) {
     const bool live = FULL || t0 + 16 * nt + n <= pos;       // the lane's A row (token 16 nt + n)
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float2 kbs = make_float2(1.f, 1.f);             // NVFP4: blocks 2 kg, 2 kg + 1 (1.0 = 0x38 where masked)
+    if constexpr (FMT == 2) kbs = e4m3x2_f32(live ? r.kb[nt] : 0x3838u);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u32x4 a;
       if constexpr (FMT == 0) {
         uint32_t w4[4];
         fp4x8_to_bf16(live ? r.k[nt][s] : 0u, e8m0_scale(live ? r.ks[nt] : 127u), w4);
+        a = u32x4{w4[0], w4[1], w4[2], w4[3]};
+      } else if constexpr (FMT == 2) {
+        uint32_t w4[4];
+        fp4x8_to_bf16_nv(live ? r.k[nt][s] : 0u, s < 2 ? kbs.x : kbs.y, w4);
         a = u32x4{w4[0], w4[1], w4[2], w4[3]};
       } else {
         const u32x4 &src = r.k[nt][s >> 1];
@@ -215,7 +249,7 @@ __device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float x = acc[i] * qk_scale2;
-      if constexpr (FMT == 1) x *= r.ks[nt][i];
+      if constexpr (FMT != 0) x *= r.ks[nt][i];
       sc[nt][i] = (FULL || t0 + 16 * nt + 4 * kg + i <= pos) ? x : NEG_INF;
     }
   }
@@ -259,7 +293,7 @@ __device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       float p0 = sc[2 * s + (h >> 1)][2 * (h & 1)], p1 = sc[2 * s + (h >> 1)][2 * (h & 1) + 1];
-      if constexpr (FMT == 1) {
+      if constexpr (FMT != 0) {
         // fold V's token scale into P; masked tokens keep p = 0 (their scale may be NaN)
         const f32x4 &vs = r.vs[s][h >> 1];
         p0 = p0 == 0.0f ? 0.0f : p0 * vs[2 * (h & 1)];
@@ -274,6 +308,9 @@ __device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t
       if constexpr (FMT == 0) {
         const uint32_t sb = __builtin_amdgcn_ubfe(r.vs[s][e >> 2][e & 3], 8 * (n >> 2), 8);
         fp4x8_to_bf16(live ? r.v[s][e] : 0u, e8m0_scale(live ? sb : 127u), W[e]);
+      } else if constexpr (FMT == 2) {
+        const uint32_t cb = __builtin_amdgcn_ubfe(r.vb[s][e], 8 * ((n >> 1) & 3), 8);   // block n / 2's code
+        fp4x8_to_bf16_nv(live ? r.v[s][e] : 0u, e4m3x2_f32(live ? cb : 0x38u).x, W[e]);
       } else {
         const uint2 x = e4m3x4_to_bf16(live ? r.v[s][e].x : 0u), y = e4m3x4_to_bf16(live ? r.v[s][e].y : 0u);
         W[e][0] = x.x;
@@ -750,8 +787,11 @@ hipError_t launch_split_attn(const CacheView &c, const void *q, int q_dtype, con
   if (c.kv_format == 0)
     hipLaunchKernelGGL(k_split_attn<0>, grid, dim3(256), 0, s, c, q, block_table, q_rows, H, topk, P, sm_scale,
                        sp_m, sp_l, sp_o);
-  else
+  else if (c.kv_format == 1)
     hipLaunchKernelGGL(k_split_attn<1>, grid, dim3(256), 0, s, c, q, block_table, q_rows, H, topk, P, sm_scale,
+                       sp_m, sp_l, sp_o);
+  else
+    hipLaunchKernelGGL(k_split_attn<2>, grid, dim3(256), 0, s, c, q, block_table, q_rows, H, topk, P, sm_scale,
                        sp_m, sp_l, sp_o);
   return hipGetLastError();
 }
@@ -770,10 +810,14 @@ static void launch_attn_items(const CacheView &c, const float *scores, const voi
     if (c.stride <= NT * 2) MXS_SELECT_ATTN(0, 2);
     else if (c.stride <= NT * 8) MXS_SELECT_ATTN(0, 8);
     else MXS_SELECT_ATTN(0, 32);
-  } else {
+  } else if (c.kv_format == 1) {
     if (c.stride <= NT * 2) MXS_SELECT_ATTN(1, 2);
     else if (c.stride <= NT * 8) MXS_SELECT_ATTN(1, 8);
     else MXS_SELECT_ATTN(1, 32);
+  } else {
+    if (c.stride <= NT * 2) MXS_SELECT_ATTN(2, 2);
+    else if (c.stride <= NT * 8) MXS_SELECT_ATTN(2, 8);
+    else MXS_SELECT_ATTN(2, 32);
   }
 #undef MXS_SELECT_ATTN
 }

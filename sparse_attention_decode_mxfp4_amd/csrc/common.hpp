@@ -2,7 +2,9 @@
 //
 // Number formats (OCP Microscaling Formats v1.0 for e2m1 / e8m0, OCP FP8 for
 // e4m3; the pages name the formats, ATOM PR #2812 "Mono decode over the MXFP4
-// KV and index caches", commit messages):
+// KV and index caches", commit messages; NVFP4 is named in ATOM PR #2686,
+// timeline entry #2744, and read as e2m1 in 16-element blocks with e4m3 block
+// scales and a per-token fp32 scale):
 //   e2m1  1 sign, 2 exponent, 1 mantissa bit: +-{0, .5, 1, 1.5, 2, 3, 4, 6}
 //   e8m0  a power of two 2^(byte - 127); byte 255 is NaN
 //   e4m3  bias 7, max 448, 0x7F / 0xFF NaN, subnormals m * 2^-9
@@ -19,6 +21,13 @@ constexpr int kMxPageBytes = 8704;     // 128 * 64 data + 128 * 4 scale bytes
 constexpr int kMxScaleOff = 8192;
 constexpr int kF8PageBytes = 16896;    // 128 * 128 codes + 128 fp32 scales
 constexpr int kF8ScaleOff = 16384;
+constexpr int kNvPageBytes = 9728;     // 128 * 64 codes + 128 * 8 e4m3 block scales + 128 fp32 token scales
+constexpr int kNvBScaleOff = 8192;
+constexpr int kNvTScaleOff = 9216;
+
+// Page bytes of a cache format (0 MXFP4, 1 FP8, 2 NVFP4).
+template <int FMT>
+constexpr int kPageBytes = FMT == 0 ? kMxPageBytes : (FMT == 1 ? kF8PageBytes : kNvPageBytes);
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
@@ -92,6 +101,37 @@ __device__ __forceinline__ void fp4x8_to_bf16(uint32_t packed, float scale_f32, 
   out[2] = bf16x2_bits(MXS_CVT_FP4_BF16(packed, scale_f32, 2));
   out[3] = bf16x2_bits(MXS_CVT_FP4_BF16(packed, scale_f32, 3));
 }
+
+// Two fp32 as a bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// The e4m3 codes in bytes 0 and 1 of `d` as fp32 (exact; 0x7F / 0xFF give NaN).
+__device__ __forceinline__ float2 e4m3x2_f32(uint32_t d) {
+  const uint32_t b = bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, false));
+  return make_float2(u2f(b << 16), u2f(b & 0xFFFF0000u));
+}
+
+// NVFP4 widening: the eight e2m1 codes of `packed` (low nibble first) times an
+// e4m3 block scale `sc` (given as its exact fp32 value) as four bf16 pairs.
+// The scaled convert instructions apply only a power of two, so the codes are
+// widened unscaled to fp32 and multiplied there: an e2m1 value has at most 2
+// significant bits and an e4m3 value at most 4, so the product (<= 6 bits,
+// between 2^-10 and 2688) is exact in fp32 and again in bf16.
+#define MXS_NV_PAIR(k)                                                       \
+  do {                                                                       \
+    const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, k); \
+    out[k] = bf16_pair(f[0] * sc, f[1] * sc);                                \
+  } while (0)
+__device__ __forceinline__ void fp4x8_to_bf16_nv(uint32_t packed, float sc, uint32_t out[4]) {
+  MXS_NV_PAIR(0);
+  MXS_NV_PAIR(1);
+  MXS_NV_PAIR(2);
+  MXS_NV_PAIR(3);
+}
+#undef MXS_NV_PAIR
 
 // Four e4m3 codes (one dword) -> two dwords of bf16 pairs, element order kept
 // (v_cvt_scalef32_pk_bf16_fp8 with scale 1: exact, e4m3 has 3 mantissa bits;

@@ -64,6 +64,9 @@ hipError_t launch_read_pages(const CacheView &c, int32_t B, uint32_t page_bytes,
   else if (page_bytes == 16896u)
     hipLaunchKernelGGL(k_read_pages<16896u>, grid, dim3(kReadThreads), 0, s, c.idx_pages, c.num_pages, c.page_table,
                        c.stride, c.context_lens, sink);
+  else if (page_bytes == 9728u)
+    hipLaunchKernelGGL(k_read_pages<9728u>, grid, dim3(kReadThreads), 0, s, c.idx_pages, c.num_pages, c.page_table,
+                       c.stride, c.context_lens, sink);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

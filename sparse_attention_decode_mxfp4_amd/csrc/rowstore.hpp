@@ -5,7 +5,8 @@
 // MXFP4 index-cache commit writes each index-key row into an 8704 B page
 // (e8m0 group scale, e2m1 elements), the main-KV commit writes K and V rows
 // with the same row store, and the e4m3 q-store commit packs the query to
-// e4m3 with unit scale, saturating.
+// e4m3 with unit scale, saturating. NVFP4 rows (named in ATOM PR #2686,
+// timeline entry #2744) follow the reading stated at nv_quant_row.
 //
 // One wave stores one 128-element row: lane l owns elements 2l and 2l+1, so a
 // 32-element group is 16 lanes and its amax is a 16-lane reduction; the wave
@@ -76,6 +77,64 @@ __device__ __forceinline__ void f8_store_row(float2 x, uint8_t *page, int tok, i
   f8_quant_row(x, codes, scale);
   st_u16<COH>(reinterpret_cast<uint16_t *>(page + 128 * tok + 2 * lane), codes);
   if (lane == 0) st_f32<COH>(reinterpret_cast<float *>(page + kF8ScaleOff + 4 * tok), scale);
+}
+
+// NVFP4 row (e2m1 in 16-element blocks, e4m3 block scales, a per-token fp32
+// scale; the public NVFP4 layout with its second-level scale kept per token):
+//   S = amax / 2688 (2688 = 6 * 448), 1 for an all-zero row, 2^-149 where the
+//   quotient underflows to 0; block b: c_b = e4m3(a_b / (6 S));
+//   code = e2m1(x / (e4m3_value(c_b) * S)), 0 where that divisor is 0;
+// every step an IEEE fp32 operation. Lane l owns elements 2l, 2l+1 of block
+// l / 8. code: the lane's code byte; cb: its block's scale code.
+__device__ __forceinline__ void nv_quant_row(float2 x, uint32_t &code, uint32_t &cb, float &S) {
+  uint32_t a = max(f2u(x.x) & 0x7FFFFFFFu, f2u(x.y) & 0x7FFFFFFFu);
+  a = max(a, xor_lane<1>(a));
+  a = max(a, xor_lane<2>(a));
+  a = max(a, xor_lane<4>(a));                                          // the 8-lane block's max
+  const float ab = u2f(a);
+  a = max(a, xor_lane<8>(a));
+  a = max(a, xor_lane<16>(a));
+  a = max(a, xor_lane<32>(a));                                         // the row's max
+  const float amax = u2f(a);
+  const float s = amax / 2688.0f;
+  S = amax == 0.0f ? 1.0f : (s == 0.0f ? u2f(1u) : s);                 // u2f(1): 2^-149
+  cb = e4m3_code(ab / (6.0f * S));
+  const float d = e4m3x2_f32(cb).x * S;
+  code = d > 0.0f ? (e2m1_code(x.x / d) | (e2m1_code(x.y / d) << 4)) : 0u;
+}
+
+// The eight block scale codes of a quantized NVFP4 row as two dwords (block k's
+// code from lane 8 k), the same in every lane.
+__device__ __forceinline__ uint2 nv_scale_words(uint32_t cb) {
+  auto rl = [&](int l) { return (uint32_t)__builtin_amdgcn_readlane((int)cb, l); };
+  return make_uint2(rl(0) | (rl(8) << 8) | (rl(16) << 16) | (rl(24) << 24),
+                    rl(32) | (rl(40) << 8) | (rl(48) << 16) | (rl(56) << 24));
+}
+
+template <bool COH = false>
+__device__ __forceinline__ void nv_store_row(float2 x, uint8_t *page, int tok, int lane) {
+  uint32_t code, cb;
+  float S;
+  nv_quant_row(x, code, cb, S);
+  st_u8<COH>(page + 64 * tok + lane, code);
+  const uint2 w = nv_scale_words(cb);
+  if (lane == 0) {
+    st_u32<COH>(reinterpret_cast<uint32_t *>(page + kNvBScaleOff + 8 * tok), w.x);
+    st_u32<COH>(reinterpret_cast<uint32_t *>(page + kNvBScaleOff + 8 * tok + 4), w.y);
+    st_f32<COH>(reinterpret_cast<float *>(page + kNvTScaleOff + 4 * tok), S);
+  }
+}
+
+// The new row x (this lane: elements 2 lane, 2 lane + 1) into token `tok` of
+// the page at `page`, in cache format `fmt`.
+template <bool COH = false>
+__device__ __forceinline__ void store_row(int fmt, float2 x, uint8_t *pool, int64_t page, int tok, int lane) {
+  if (fmt == 0)
+    mx_store_row<COH>(x, pool + page * kMxPageBytes, tok, lane);
+  else if (fmt == 1)
+    f8_store_row<COH>(x, pool + page * kF8PageBytes, tok, lane);
+  else
+    nv_store_row<COH>(x, pool + page * kNvPageBytes, tok, lane);
 }
 
 __device__ __forceinline__ float load_q_elem(const void *q, int q_dtype, int64_t i) {

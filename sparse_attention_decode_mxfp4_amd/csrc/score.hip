@@ -22,7 +22,7 @@ static void launch_mt(const CacheView &c, const uint16_t *q_idx, const float *w,
       launch_shape<FMT, MT, Shape<4, 2, 2>>(c, q_idx, w, B, q, H_I, scores, st, s);
     else
       launch_shape<FMT, MT, Shape<4, 1, 2>>(c, q_idx, w, B, q, H_I, scores, st, s);
-  } else if (pages >= 256 * 32) {         // >= 256 workgroups of 32 pages
+  } else if (pages >= 256 * 32) {         // >= 256 workgroups of 32 pages (MXFP4; NVFP4 takes the same shapes)
     launch_shape<FMT, MT, Shape<4, 8, 3>>(c, q_idx, w, B, q, H_I, scores, st, s);
   } else if (pages >= 256 * 16) {
     launch_shape<FMT, MT, Shape<4, 4, 2>>(c, q_idx, w, B, q, H_I, scores, st, s);
@@ -46,8 +46,10 @@ hipError_t launch_index_score(const CacheView &c, const uint16_t *q_idx, const f
                               int32_t q, int32_t H_I, float *scores, const StepStore &st, hipStream_t s) {
   if (c.idx_format == 0)
     launch_fmt<0>(c, q_idx, w, B, q, H_I, scores, st, s);
-  else
+  else if (c.idx_format == 1)
     launch_fmt<1>(c, q_idx, w, B, q, H_I, scores, st, s);
+  else
+    launch_fmt<2>(c, q_idx, w, B, q, H_I, scores, st, s);
   return hipGetLastError();
 }
 

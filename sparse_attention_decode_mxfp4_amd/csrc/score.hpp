@@ -12,7 +12,9 @@
 // N = 16 tokens, K = head_dim. The page's e2m1 keys are widened to bf16 in
 // registers with their e8m0 group scale (v_cvt_scalef32_pk_bf16_fp4; bf16
 // holds every e2m1 value times a power of two exactly, so the products are
-// exact and only the fp32 accumulation rounds).
+// exact and only the fp32 accumulation rounds). FP8 keys widen exactly to
+// bf16 and NVFP4 keys to bf16 times their e4m3 block scale (exact as well);
+// both apply the token's fp32 scale to the dot product.
 //
 // Lane layout (lane = 16 kg + n): for an N-tile of 16 tokens the lane takes
 // the 16 bytes of token n's group kg — one 32-element group and its one scale
@@ -42,12 +44,15 @@ typedef __attribute__((address_space(1))) void *glb_ptr_t;
 // while chunk u is computed. Each lane reads back exactly the bytes it copied.
 // Lane (n, kg) of the chunk's tile nt (token 64 h + 16 nt + n of the page,
 // h = half):
-//   MXFP4: codes of group kg (16 B) at stage + 1024 nt + 16 lane;
+//   MXFP4, NVFP4: codes of group kg (16 B) at stage + 1024 nt + 16 lane;
 //   FP8:   codes 32 kg .. 32 kg + 31 (2 x 16 B) at stage + 1024 (2 nt + c) + 16 lane.
-// The chunk's 256 B of per-token scales follow the codes (4096 or 8192 B in).
+// The chunk's 256 B of per-token scales follow the codes (4096 or 8192 B in);
+// NVFP4 puts the 64 tokens' 512 B of e4m3 block scales there (8 per token, in
+// page order) and the 256 B of fp32 token scales after them.
 template <int FMT> struct Chunk;
 template <> struct Chunk<0> { static constexpr int kCodes = 4096, kBytes = 4096 + 256, kDma = 5, kPage = kMxPageBytes, kScale = kMxScaleOff; };
 template <> struct Chunk<1> { static constexpr int kCodes = 8192, kBytes = 8192 + 256, kDma = 9, kPage = kF8PageBytes, kScale = kF8ScaleOff; };
+template <> struct Chunk<2> { static constexpr int kCodes = 4096, kTok = 4096 + 512, kBytes = 4096 + 512 + 256, kDma = 7, kPage = kNvPageBytes; };
 
 // Launch shapes: waves per workgroup, pages per wave, LDS stages per wave.
 // Measured on MI355X (MXFP4 index, 4 sequences): 4 x 8 x 3 is fastest once
@@ -96,21 +101,30 @@ __device__ __forceinline__ float max16_dpp(float v) {
 
 template <int FMT>
 __device__ __forceinline__ void dma_chunk(uint8_t *stage, const uint8_t *page, int h, int n, int kg, int lane) {
-  if constexpr (FMT == 0) {
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-      __builtin_amdgcn_global_load_lds((glb_ptr_t)(page + 64 * (64 * h + 16 * nt + n) + 16 * kg),
-                                       (lds_ptr_t)(stage + 1024 * nt), 16, 0, 0);
-  } else {
+  if constexpr (FMT == 1) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
         __builtin_amdgcn_global_load_lds((glb_ptr_t)(page + 128 * (64 * h + 16 * nt + n) + 32 * kg + 16 * cc),
                                          (lds_ptr_t)(stage + 1024 * (2 * nt + cc)), 16, 0, 0);
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)(page + 64 * (64 * h + 16 * nt + n) + 16 * kg),
+                                       (lds_ptr_t)(stage + 1024 * nt), 16, 0, 0);
   }
-  __builtin_amdgcn_global_load_lds((glb_ptr_t)(page + Chunk<FMT>::kScale + 256 * h + 4 * lane),
-                                   (lds_ptr_t)(stage + Chunk<FMT>::kCodes), 4, 0, 0);
+  if constexpr (FMT == 2) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)(page + kNvBScaleOff + 512 * h + 256 * c + 4 * lane),
+                                       (lds_ptr_t)(stage + Chunk<2>::kCodes + 256 * c), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_ptr_t)(page + kNvTScaleOff + 256 * h + 4 * lane),
+                                     (lds_ptr_t)(stage + Chunk<2>::kTok), 4, 0, 0);
+  } else {
+    __builtin_amdgcn_global_load_lds((glb_ptr_t)(page + Chunk<FMT>::kScale + 256 * h + 4 * lane),
+                                     (lds_ptr_t)(stage + Chunk<FMT>::kCodes), 4, 0, 0);
+  }
 }
 
 // B operand (k-step s) of tile nt: the lane's key elements 32 kg + 8 s .. + 7 as bf16.
@@ -127,6 +141,17 @@ __device__ __forceinline__ void key_operands(const uint8_t *stage, int nt, int n
       Bk[s] = __builtin_bit_cast(bf16x8, u32x4{w4[0], w4[1], w4[2], w4[3]});
     }
     ksc = 1.0f;
+  } else if constexpr (FMT == 2) {
+    const u32x4 kd = *reinterpret_cast<const u32x4 *>(stage + 1024 * nt + 16 * lane);
+    // the e4m3 scales of blocks 2 kg and 2 kg + 1 of token 16 nt + n
+    const float2 bs = e4m3x2_f32(*reinterpret_cast<const uint16_t *>(stage + Chunk<2>::kCodes + 8 * (16 * nt + n) + 2 * kg));
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint32_t w4[4];
+      fp4x8_to_bf16_nv(kd[s], s < 2 ? bs.x : bs.y, w4);
+      Bk[s] = __builtin_bit_cast(bf16x8, u32x4{w4[0], w4[1], w4[2], w4[3]});
+    }
+    ksc = *reinterpret_cast<const float *>(stage + Chunk<2>::kTok + 4 * (16 * nt + n));
   } else {
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
@@ -180,10 +205,7 @@ __device__ __forceinline__ void side_row(const CacheView &c, const StepStore &st
   if (page < 0 || page >= c.num_pages) return;
   const bool kv = st.k_new && r < 2 * q;
   uint8_t *pool = kv ? (r < q ? c.k_pages : c.v_pages) : c.idx_pages;
-  if ((kv ? c.kv_format : c.idx_format) == 0)
-    mx_store_row<COH>(x, pool + (int64_t)page * kMxPageBytes, t % kTokens, lane);
-  else
-    f8_store_row<COH>(x, pool + (int64_t)page * kF8PageBytes, t % kTokens, lane);
+  store_row<COH>(kv ? c.kv_format : c.idx_format, x, pool, page, t % kTokens, lane);
 }
 
 // first-round sources (no dependence on the context length)
@@ -213,19 +235,29 @@ __device__ __forceinline__ void side_finish(const CacheView &c, const StepStore 
 }
 
 // A new row quantized by one wave (this lane: elements 2 lane, 2 lane + 1):
-// code = the lane's code byte (MXFP4) or byte pair (FP8); gsb = the e8m0 byte
-// of the lane's 32-element group (MXFP4); word = the token's scale dword as
-// the page holds it (MXFP4: the four group bytes; FP8: the fp32 scale bits).
+// code = the lane's code byte (MXFP4, NVFP4) or byte pair (FP8); word = the
+// token's scale dwords as the page holds them (MXFP4: the four group bytes;
+// FP8: the fp32 scale bits; NVFP4: the eight block scale codes, then the fp32
+// token scale bits).
+template <int FMT> constexpr int kRowWords = FMT == 2 ? 3 : 1;
 template <int FMT>
-__device__ __forceinline__ void quant_row(float2 x, uint32_t &code, uint32_t &gsb, uint32_t &word) {
+__device__ __forceinline__ void quant_row(float2 x, uint32_t &code, uint32_t (&word)[kRowWords<FMT>]) {
   if constexpr (FMT == 0) {
+    uint32_t gsb;
     mx_quant_row(x, code, gsb);
-    word = mx_scale_word(gsb);
-  } else {
+    word[0] = mx_scale_word(gsb);
+  } else if constexpr (FMT == 1) {
     float scale;
     f8_quant_row(x, code, scale);
-    gsb = 0u;
-    word = f2u(scale);
+    word[0] = f2u(scale);
+  } else {
+    uint32_t cb;
+    float S;
+    nv_quant_row(x, code, cb, S);
+    const uint2 w = nv_scale_words(cb);
+    word[0] = w.x;
+    word[1] = w.y;
+    word[2] = f2u(S);
   }
 }
 
@@ -239,26 +271,35 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
   return (uint32_t)(uintptr_t)(lds_ptr_t)const_cast<uint8_t *>(p);
 }
 template <int FMT>
-__device__ __forceinline__ void patch_row(uint8_t *stage, int tc, uint32_t code, uint32_t word, int lane) {
+__device__ __forceinline__ void patch_row(uint8_t *stage, int tc, uint32_t code, const uint32_t *word, int lane) {
   const int nt = tc >> 4, nn = tc & 15;
   if constexpr (FMT == 0) {
     asm volatile("ds_write_b8 %0, %1" ::"v"(lds_addr(stage + 1024 * nt + 256 * (lane >> 4) + 16 * nn + (lane & 15))),
                  "v"(code) : "memory");
     if (lane == 0)
-      asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(stage + Chunk<0>::kCodes + 4 * tc)), "v"(word) : "memory");
+      asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(stage + Chunk<0>::kCodes + 4 * tc)), "v"(word[0]) : "memory");
+  } else if constexpr (FMT == 2) {
+    asm volatile("ds_write_b8 %0, %1" ::"v"(lds_addr(stage + 1024 * nt + 256 * (lane >> 4) + 16 * nn + (lane & 15))),
+                 "v"(code) : "memory");
+    if (lane == 0) {
+      asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(stage + Chunk<2>::kCodes + 8 * tc)), "v"(word[0]) : "memory");
+      asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(stage + Chunk<2>::kCodes + 8 * tc + 4)), "v"(word[1])
+                   : "memory");
+      asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(stage + Chunk<2>::kTok + 4 * tc)), "v"(word[2]) : "memory");
+    }
   } else {
     asm volatile("ds_write_b16 %0, %1" ::"v"(lds_addr(stage + 1024 * (2 * nt + ((lane & 15) >> 3)) +
                                                         16 * (16 * (lane >> 4) + nn) + 2 * (lane & 7))),
                  "v"(code) : "memory");
     if (lane == 0)
-      asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(stage + Chunk<1>::kCodes + 4 * tc)), "v"(word) : "memory");
+      asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(stage + Chunk<1>::kCodes + 4 * tc)), "v"(word[0]) : "memory");
   }
 }
 
 // LDS bytes of one scoring workgroup: the waves' stage rings, then the step's
-// new index rows quantized (4 MT rows: 64 lane words, then one scale word each).
+// new index rows quantized (4 MT rows: 64 lane words, then the scale words).
 template <int MT, int FMT, int NW, int S>
-constexpr int kScoreLds = NW * S * Chunk<FMT>::kBytes + 4 * MT * 65 * 4;
+constexpr int kScoreLds = NW * S * Chunk<FMT>::kBytes + 4 * MT * (64 + kRowWords<FMT>) * 4;
 
 // One scoring workgroup: sequence b, wave group gy of ny. lds: kScoreLds bytes,
 // 16-byte aligned, the workgroup's only LDS object while it scores (a second
@@ -275,7 +316,7 @@ __device__ __forceinline__ void index_score_wg(const CacheView &c, const uint16_
   static_assert(S >= 2 && S - 1 <= kUnits, "stage ring");
   auto stage_at = [&](int w, int u) { return lds + (w * S + u) * CK::kBytes; };
   uint32_t *s_qc = reinterpret_cast<uint32_t *>(lds + NW * S * CK::kBytes);   // [4 MT][64]
-  uint32_t *s_qw = s_qc + 4 * MT * 64;                                        // [4 MT]
+  uint32_t *s_qw = s_qc + 4 * MT * 64;                                        // [4 MT][kRowWords]
   // grid (sequence, wave group). Waves are numbered in dispatch order, d, and
   // take the sequence's pages from the back (d = 0: the last pages, where the
   // step's new rows are, so the wave with the most extra work starts first);
@@ -365,10 +406,12 @@ __device__ __forceinline__ void index_score_wg(const CacheView &c, const uint16_
     for (int k = 0; k < kOwnRows; ++k) {
       const int j = wave + NW * k;
       if (j >= 4 * MT) continue;
-      uint32_t code, gsb, word;
-      quant_row<FMT>(xr[k], code, gsb, word);
+      uint32_t code, word[kRowWords<FMT>];
+      quant_row<FMT>(xr[k], code, word);
       s_qc[64 * j + lane] = code;
-      if (lane == 0) s_qw[j] = word;
+      if (lane == 0)
+#pragma unroll
+        for (int i = 0; i < kRowWords<FMT>; ++i) s_qw[kRowWords<FMT> * j + i] = word[i];
     }
     // LDS writes done, then the workgroup barrier (no wait for the copies)
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -407,7 +450,7 @@ __device__ __forceinline__ void index_score_wg(const CacheView &c, const uint16_
           for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][s], Bk[s], acc, 0, 0, 0);
           float v = 0.f;
 #pragma unroll
-          for (int hd = 0; hd < 4; ++hd) v += wv[mt][hd] * relu1(FMT == 1 ? acc[hd] * ksc : acc[hd]);
+          for (int hd = 0; hd < 4; ++hd) v += wv[mt][hd] * relu1(FMT != 0 ? acc[hd] * ksc : acc[hd]);
           rmax[mt] = fmaxf(rmax[mt], (full || (t >= t_lo && t <= hi[mt])) ? v : NEG_INF);
         }
       }
@@ -453,7 +496,8 @@ __device__ __forceinline__ void index_score_wg(const CacheView &c, const uint16_
 #pragma unroll
         for (int j = 0; j < 4 * MT; ++j) {
           const int t = L - q + j;
-          if (j < q && t >= c0 && t <= c0 + 63) patch_row<FMT>(stage, t - c0, s_qc[64 * j + lane], s_qw[j], lane);
+          if (j < q && t >= c0 && t <= c0 + 63)
+            patch_row<FMT>(stage, t - c0, s_qc[64 * j + lane], s_qw + kRowWords<FMT> * j, lane);
         }
       }
       if (h == 0) {

@@ -7,7 +7,8 @@
 // (e8m0 group scale, e2m1 elements), the main-KV commit writes K and V rows
 // with the same row store, and the e4m3 q-store commit packs the query to
 // e4m3 with unit scale, saturating (the pack_q_e4m3 commit: beyond +-448 and
-// inf saturate, NaN stays NaN).
+// inf saturate, NaN stays NaN). NVFP4 rows follow the reading stated in
+// rowstore.hpp (nv_quant_row).
 //
 // One wave stores one 128-element row: lane l owns elements 2l and 2l+1, so a
 // 32-element group is 16 lanes and its amax is a 16-lane reduction; the wave
@@ -30,12 +31,7 @@ __global__ __launch_bounds__(256) void k_row_store(const float *__restrict__ row
   const int64_t slot = slots[r];
   if (slot < 0 || slot >= (int64_t)num_pages * kTokens) return;
   const float2 x = reinterpret_cast<const float2 *>(rows + r * kDim)[lane];
-  const int64_t page = slot / kTokens;
-  const int tok = (int)(slot % kTokens);
-  if (FMT == 0)
-    mx_store_row(x, pages + page * kMxPageBytes, tok, lane);
-  else
-    f8_store_row(x, pages + page * kF8PageBytes, tok, lane);
+  store_row(FMT, x, pages, slot / kTokens, (int)(slot % kTokens), lane);
 }
 
 __global__ __launch_bounds__(256) void k_pack_q(const void *__restrict__ q, int q_dtype, int64_t n,
@@ -67,11 +63,7 @@ __global__ __launch_bounds__(256) void k_reuse_store(CacheView c, const float *_
     if (pos < 0 || pos / kTokens >= c.stride) return;
     const int phys = c.page_table[(int64_t)b * c.stride + pos / kTokens];
     if (phys < 0 || phys >= c.num_pages) return;
-    uint8_t *pool = wave == 0 ? c.k_pages : c.v_pages;
-    if (c.kv_format == 0)
-      mx_store_row(x, pool + (int64_t)phys * kMxPageBytes, pos % kTokens, lane);
-    else
-      f8_store_row(x, pool + (int64_t)phys * kF8PageBytes, pos % kTokens, lane);
+    store_row(c.kv_format, x, wave == 0 ? c.k_pages : c.v_pages, phys, pos % kTokens, lane);
   } else if (q8) {
     // elements e0 .. e0 + 15 of the row (H x 128 <= 2048 = 16 x 128 threads);
     // the query is 16-byte aligned, so are the row and each thread's run
@@ -131,8 +123,10 @@ hipError_t launch_row_store(int format, const float *rows, int64_t n, const int6
   const dim3 grid((unsigned)((n + 3) / 4));
   if (format == 0)
     hipLaunchKernelGGL(k_row_store<0>, grid, dim3(256), 0, s, rows, n, slots, pages, num_pages);
-  else
+  else if (format == 1)
     hipLaunchKernelGGL(k_row_store<1>, grid, dim3(256), 0, s, rows, n, slots, pages, num_pages);
+  else
+    hipLaunchKernelGGL(k_row_store<2>, grid, dim3(256), 0, s, rows, n, slots, pages, num_pages);
   return hipGetLastError();
 }
 

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_stages():
     names = declared_functions()
-    for f in ["mxfp4_row_store", "fp8_row_store", "pack_q_e4m3", "index_score", "topk_blocks",
+    for f in ["mxfp4_row_store", "fp8_row_store", "nvfp4_row_store", "pack_q_e4m3", "index_score", "topk_blocks",
               "index_score_topk", "sparse_split_attn", "lse_merge", "decode_step", "decode_step_reuse",
               "mxs_workspace_bytes",
               "mxs_default_partitions", "mxs_status_str", "mxs_last_error", "mxs_abi_version",
@@ -75,6 +75,9 @@ def test_row_store_rejects_before_launch(L):
     assert "rows" in _err(L)
     assert L.fp8_row_store(ctypes.c_void_p(256), 4, ctypes.c_void_p(256), ctypes.c_void_p(3), 1, None) == mx.MXS_EINVAL
     assert "16-byte" in _err(L)
+    assert L.nvfp4_row_store(ctypes.c_void_p(256), 4, ctypes.c_void_p(260), ctypes.c_void_p(256), 1, None) == \
+        mx.MXS_EINVAL
+    assert "nvfp4_row_store" in _err(L) and "slots" in _err(L)
 
 
 def test_pack_q_rejects_dtype(L):
@@ -91,10 +94,11 @@ def _cache(**kw):
 def test_refusal_matrix(L):
     P = ctypes.byref
     good_q, good_w = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
-    # unsupported formats (NVFP4 and anything else) are refused by name
-    c = _cache(idx_format=2)
-    assert L.index_score(P(c), good_q, good_w, 1, 1, 4, ctypes.c_void_p(256), None) == mx.MXS_EUNSUPPORTED
-    assert "NVFP4" in _err(L)
+    # format ids other than MXFP4 = 0, FP8 = 1 and NVFP4 = 2 are refused, naming the accepted ones
+    for bad in (3, -1):
+        c = _cache(idx_format=bad)
+        assert L.index_score(P(c), good_q, good_w, 1, 1, 4, ctypes.c_void_p(256), None) == mx.MXS_EUNSUPPORTED
+        assert "NVFP4 = 2" in _err(L)
     c = _cache()
     assert L.index_score(P(c), good_q, good_w, 1, 1, 5, ctypes.c_void_p(256), None) == mx.MXS_EUNSUPPORTED
     assert L.index_score(P(c), good_q, good_w, 1, 17, 4, ctypes.c_void_p(256), None) == mx.MXS_EUNSUPPORTED
@@ -108,8 +112,12 @@ def test_refusal_matrix(L):
     assert L.sparse_split_attn(*args(c, mx.MXS_E4M3, 17, 1)) == mx.MXS_EUNSUPPORTED
     assert L.sparse_split_attn(*args(c, mx.MXS_E4M3, 16, 65)) == mx.MXS_EUNSUPPORTED
     assert L.sparse_split_attn(*args(c, mx.MXS_BF16, 16, 1)) == mx.MXS_EUNSUPPORTED
-    assert "e4m3" in _err(L)
-    assert L.sparse_split_attn(*args(_cache(kv_format=1), mx.MXS_E4M3, 16, 1)) == mx.MXS_EUNSUPPORTED
+    assert L.sparse_split_attn(*args(_cache(kv_format=3), mx.MXS_BF16, 16, 1)) == mx.MXS_EUNSUPPORTED
+    assert "kv_format" in _err(L)
+    # FP8 and NVFP4 K/V take a bf16 query, not e4m3 codes
+    for f in (1, 2):
+        assert L.sparse_split_attn(*args(_cache(kv_format=f), mx.MXS_E4M3, 16, 1)) == mx.MXS_EUNSUPPORTED
+        assert "bf16 query" in _err(L)
     assert L.sparse_split_attn(*args(_cache(k_pages=0), mx.MXS_E4M3, 16, 1)) == mx.MXS_EINVAL
     assert L.lse_merge(ctypes.c_void_p(256), ctypes.c_void_p(256), ctypes.c_void_p(256), 1, 65,
                        ctypes.c_void_p(256), None, None) == mx.MXS_EUNSUPPORTED
@@ -161,7 +169,7 @@ def test_read_index_pages_rejects_before_launch(L):
     assert L.mxs_read_index_pages(P(_cache()), 1, ctypes.c_void_p(258), None) == mx.MXS_EINVAL
     assert L.mxs_read_index_pages(P(_cache()), -1, sink, None) == mx.MXS_EINVAL
     assert L.mxs_read_index_pages(P(_cache(idx_pages=0)), 1, sink, None) == mx.MXS_EINVAL
-    assert L.mxs_read_index_pages(P(_cache(idx_format=2)), 1, sink, None) == mx.MXS_EUNSUPPORTED
+    assert L.mxs_read_index_pages(P(_cache(idx_format=3)), 1, sink, None) == mx.MXS_EUNSUPPORTED
     assert L.mxs_read_index_pages(P(_cache()), 0, sink, None) == mx.MXS_OK    # nothing to read
 
 

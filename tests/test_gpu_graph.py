@@ -38,7 +38,7 @@ def _setup(name):
     return inp, WG.make_cache(inp, pools), WG.step_tensors(inp)
 
 
-@pytest.mark.parametrize("name", ["mxfp4_65k", "fp8", "one_launch"])
+@pytest.mark.parametrize("name", ["mxfp4_65k", "fp8", "nvfp4", "one_launch"])
 def test_decode_step_graph_replays_equal_eager(mx, name):
     inp, cache, t = _setup(name)
     wl = inp.wl

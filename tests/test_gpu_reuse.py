@@ -77,7 +77,7 @@ def check_reuse(inp, g, table, seqs):
         assert (np.isneginf(g["lse"][b]) == np.isneginf(r["lse"][b])).all()
 
 
-@pytest.mark.parametrize("name", ["tiny", "fp8", "mxfp4_65k"])
+@pytest.mark.parametrize("name", ["tiny", "fp8", "mxfp4_65k", "nvfp4"])
 def test_reuse_step_small(mx, name):
     inp = W.make_inputs(W.WORKLOADS[name])
     table = random_table(inp, 11)
@@ -85,7 +85,7 @@ def test_reuse_step_small(mx, name):
     check_reuse(inp, g, table, range(inp.wl.B))
 
 
-@pytest.mark.parametrize("name", ["tiny", "fp8", "mxfp4_65k", "one_launch"])
+@pytest.mark.parametrize("name", ["tiny", "fp8", "mxfp4_65k", "nvfp4", "one_launch"])
 def test_reuse_step_on_the_full_steps_selection_is_bitwise_the_full_step(mx, name):
     """decode_step, then decode_step_reuse over the block table it wrote, from
     the same pre-step caches: identical output, lse and K / V pages (also after

@@ -54,12 +54,45 @@ def _tricky_rows(n, seed):
     return x
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "fp8"])
+def _tricky_nv_rows(n, seed):
+    """fp32 rows for the NVFP4 row store: wide exponents; half the rows on the
+    format's grid with elements on e2m1 tie points (token scale a power of two,
+    block 0 holding 6 * 448 of it, every block's scale an exact e4m3 value), so
+    every division lands exactly on a tie; a zero row, an all -0 row, zero and
+    sub-range blocks, a row of fp32 subnormals (token scale clamped at 2^-149)
+    and values near the fp32 maximum."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, 128)).astype(np.float32)
+    x *= np.ldexp(1.0, rng.integers(-60, 60, size=(n, 1))).astype(np.float32)
+    x[rng.random((n, 128)) < 0.01] *= np.float32(20.0)
+    sel = np.flatnonzero(rng.random(n) < 0.5)
+    m = sel.size
+    S = np.ldexp(1.0, rng.integers(-40, 40, size=(m, 1, 1)))
+    cb = OF.E4M3_TABLE[rng.integers(1, 127, size=(m, 8, 1))]
+    cb[:, 0] = 448.0
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.0, 6.0, 4.0, 0.5])
+    v = rng.choice(mids, size=(m, 8, 16)) * rng.choice([-1.0, 1.0], size=(m, 8, 16))
+    v[:, :, 0] = 6.0
+    x[sel] = (v * cb * S).reshape(m, 128).astype(np.float32)
+    x[0] = 0.0
+    x[1] = -0.0
+    x[2, 16:32] = 0.0
+    x[2, 48:64] *= np.float32(1e-7)
+    with np.errstate(under="ignore"):
+        x[3] = (rng.standard_normal(128) * 1e-41).astype(np.float32)
+    x[4] = rng.uniform(-3e38, 3e38, 128).astype(np.float32)
+    return x
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "fp8", "nvfp4"])
 def test_row_store_bit_exact(mx, fmt):
-    n = (1 << 20) if fmt == "mxfp4" else (1 << 17)
-    x = _tricky_rows(n, 7) if fmt == "mxfp4" else \
-        np.random.default_rng(8).standard_normal((n, 128)).astype(np.float32) * 3
-    if fmt == "fp8":
+    n = {"mxfp4": 1 << 20, "fp8": 1 << 17, "nvfp4": 1 << 18}[fmt]
+    if fmt == "mxfp4":
+        x = _tricky_rows(n, 7)
+    elif fmt == "nvfp4":
+        x = _tricky_nv_rows(n, 12)
+    else:
+        x = np.random.default_rng(8).standard_normal((n, 128)).astype(np.float32) * 3
         x[0] = 0.0
         x[1, 5] = 1e4
     pages = (n + 127) // 128
@@ -70,7 +103,7 @@ def test_row_store_bit_exact(mx, fmt):
     t = np.arange(n)
     slots = table[t // 128].astype(np.int64) * 128 + t % 128
     pool = torch.full((num_pages * OF.PAGE_BYTES[fmt],), 0xFF, dtype=torch.uint8, device=DEV)
-    store = mx.mxfp4_row_store if fmt == "mxfp4" else mx.fp8_row_store
+    store = {"mxfp4": mx.mxfp4_row_store, "fp8": mx.fp8_row_store, "nvfp4": mx.nvfp4_row_store}[fmt]
     store(torch.from_numpy(x).to(DEV), torch.from_numpy(slots).to(DEV), pool)
     got = pool.cpu().numpy()
     PT.compare_pool_pages(got, ref, np.arange(num_pages), OF.PAGE_BYTES[fmt], f"{fmt} row store")
@@ -129,7 +162,7 @@ def _setup(mx, name, **kw):
     return inp, pools, cache, WG.step_tensors(inp)
 
 
-SMALL = ["tiny", "fp8", "mxfp4_65k"]
+SMALL = ["tiny", "fp8", "mxfp4_65k", "nvfp4"]
 
 
 @pytest.mark.parametrize("name", SMALL)

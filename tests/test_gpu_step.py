@@ -79,7 +79,7 @@ def check_step(inp, g, seqs):
     assert n_equal >= 0.9 * n_rows, f"only {n_equal}/{n_rows} rows select the oracle's exact set"
 
 
-@pytest.mark.parametrize("name", ["tiny", "fp8", "mxfp4_65k"])
+@pytest.mark.parametrize("name", ["tiny", "fp8", "mxfp4_65k", "nvfp4"])
 def test_decode_step_small(mx, name):
     inp = W.make_inputs(W.WORKLOADS[name])
     g = run_step(mx, inp)
@@ -185,10 +185,13 @@ def test_decode_step_long_with_empty_partitions(mx, b):
     # 4 x 8 pages (32-page workgroups; 8192 pages in all): boundaries at 4096-token multiples
     dict(B=4, ctx_rule=("list", (262144, 4100, 8196, 65540)), topk=32),
 ])
-def test_decode_step_new_rows_straddle_scorer_workgroups(mx, kw):
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_decode_step_new_rows_straddle_scorer_workgroups(mx, kw, fmt):
     """The step's new index rows split between two scorer workgroups, in each
-    of the scorer's launch shapes for MXFP4 pages."""
-    wl = W.WORKLOADS["mxfp4_65k"].with_(name="straddle", **kw)
+    of the scorer's launch shapes for MXFP4 pages (NVFP4 pages take the same
+    shapes)."""
+    wl = W.WORKLOADS["mxfp4_65k"].with_(name="straddle", kv_format=fmt, idx_format=fmt,
+                                        q_dtype="f32" if fmt == "mxfp4" else "bf16", **kw)
     inp = W.make_inputs(wl)
     g = run_step(mx, inp)
     check_step(inp, g, range(wl.B))
@@ -210,6 +213,24 @@ def test_decode_step_fp8_65k(mx):
     check_step(inp, g, range(inp.wl.B))
 
 
+def test_decode_step_nvfp4_65k(mx):
+    """The NVFP4 workload at 65536 - u tokens (2048 pages in all, the last
+    page of each sequence partly filled and NaN-poisoned past it)."""
+    inp, g = cached_run(mx, "nvfp4", ctx_rule=("fixed_minus_u", 65536, 127))
+    check_step(inp, g, range(inp.wl.B))
+
+
+@pytest.mark.parametrize("kv,idx", [("nvfp4", "mxfp4"), ("mxfp4", "nvfp4"), ("fp8", "nvfp4"), ("nvfp4", "fp8")])
+def test_decode_step_mixed_formats(mx, kv, idx):
+    """K / V pages in one format and index pages in another (each cache slot
+    takes its own format id)."""
+    wl = W.WORKLOADS["mxfp4_65k"].with_(name=f"mixed_{kv}_{idx}", B=2, kv_format=kv, idx_format=idx,
+                                        q_dtype="f32" if kv == "mxfp4" else "bf16")
+    inp = W.make_inputs(wl)
+    g = run_step(mx, inp)
+    check_step(inp, g, range(wl.B))
+
+
 # "one_launch": the 65K workload with 2048-entry page tables (B x stride =
 # 8192 pages, which decode_step_one_launch takes) run through that entry point
 def _wl(name):
@@ -218,7 +239,7 @@ def _wl(name):
     return W.WORKLOADS[name].with_(B=4)
 
 
-@pytest.mark.parametrize("name", ["mxfp4_65k", "fp8", "one_launch"])
+@pytest.mark.parametrize("name", ["mxfp4_65k", "fp8", "nvfp4", "one_launch"])
 def test_decode_step_repeats_bit_exact(mx, name):
     """The same step run many times gives bit-identical output and lse: each
     row is merged by whichever of its partition workgroups finishes last, from

@@ -31,7 +31,7 @@ def fill_prefix(inp: StepInputs, pools, seqs=None, chunk_rows=1 << 20, device="c
     library's row store."""
     wl = inp.wl
     fmts = {"k": wl.kv_format, "v": wl.kv_format, "idx": wl.idx_format}
-    store = {"mxfp4": mx.mxfp4_row_store, "fp8": mx.fp8_row_store}
+    store = {"mxfp4": mx.mxfp4_row_store, "fp8": mx.fp8_row_store, "nvfp4": mx.nvfp4_row_store}
     jobs = [(s, b) for s in STREAMS for b in (range(wl.B) if seqs is None else seqs)]
     with ThreadPoolExecutor(max_workers=8) as ex:          # numpy draws release the GIL
         for (s, b), rows in zip(jobs, ex.map(lambda sb: inp.rows(*sb), jobs)):
