@@ -38,35 +38,45 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 PAGE_MX = 8704
+# page bytes and bytes of one stored 128-element row, per cache format
+PAGE_BYTES = {"mxfp4": 8704, "fp8": 16896, "nvfp4": 9728}
+ROW_BYTES = {"mxfp4": 64 + 4, "fp8": 128 + 4, "nvfp4": 64 + 8 + 4}
 CSRC = os.path.join(ROOT, "sparse_attention_decode_mxfp4_amd", "csrc")
 # the sources the index scorer kernel is built from; the HBM traffic measured
 # with rocprofv3 counters is reported only while they are unchanged
-SCORER_SOURCES = ("score.hip", "common.hpp", "rowstore.hpp", "launch.hpp")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scorer_traffic.json")
+SCORER_SOURCES = ("score.hip", "score.hpp", "common.hpp", "rowstore.hpp", "launch.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scorer_traffic_{}.json")      # per workload
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def query_bytes(wl) -> int:
+    """Bytes of one attention-query element as the step reads it."""
+    return 4 if (wl.kv_format == "mxfp4" and wl.q_dtype == "f32") else 2
+
+
 def algorithmic_bytes(inp, table: np.ndarray) -> dict:
     """Bytes the step must move at minimum: every index page of every sequence
     once, the distinct K and V pages the sequence's rows selected, the new rows
-    (read as fp32, stored as MXFP4), the query, index query, weights, page table
-    and the bf16 output with its lse."""
+    (read as fp32, stored in the cache formats), the query, index query,
+    weights, page table and the bf16 output with its lse."""
     wl = inp.wl
     idx_pages = int(sum((int(L) + 127) // 128 for L in inp.contexts))
     kv_pages = 0
     for b in range(wl.B):
         kv_pages += len(np.unique(table[b][table[b] >= 0]))
     rows = wl.B * wl.q
-    other = (3 * rows * 128 * 4 + 3 * rows * 68            # new rows in, stored rows out
-             + rows * wl.H * 128 * 4                      # fp32 query
+    pi, pkv = PAGE_BYTES[wl.idx_format], PAGE_BYTES[wl.kv_format]
+    other = (3 * rows * 128 * 4                           # new rows in
+             + 2 * rows * ROW_BYTES[wl.kv_format] + rows * ROW_BYTES[wl.idx_format]   # stored rows out
+             + rows * wl.H * 128 * query_bytes(wl)        # query
              + rows * wl.H_I * 128 * 2 + rows * wl.H_I * 4  # index query, weights
              + wl.B * inp.max_pages * 4 + wl.B * 4        # page table, contexts
              + rows * wl.H * 128 * 2 + rows * wl.H * 4)   # output bf16, lse
-    return {"index_pages": idx_pages * PAGE_MX, "kv_pages": 2 * kv_pages * PAGE_MX, "other": other,
-            "total": idx_pages * PAGE_MX + 2 * kv_pages * PAGE_MX + other,
+    return {"index_pages": idx_pages * pi, "kv_pages": 2 * kv_pages * pkv, "other": other,
+            "total": idx_pages * pi + 2 * kv_pages * pkv + other,
             "n_index_pages": idx_pages, "n_kv_pages": 2 * kv_pages}
 
 
@@ -84,7 +94,7 @@ def measured_traffic(workload: str):
     (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy's reading), or None
     when there is none for this workload or the scorer changed since."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(TRAFFIC_FILE.format(workload)) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
@@ -348,7 +358,8 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     reuse_us = ev0.elapsed_time(ev1) * 1e3 / (n_rep * R)
-    reuse_bytes = (ab["kv_pages"] + 2 * rows * 128 * 4 + 2 * rows * 68 + rows * wl.H * 128 * 4
+    reuse_bytes = (ab["kv_pages"] + 2 * rows * 128 * 4 + 2 * rows * ROW_BYTES[wl.kv_format]
+                   + rows * wl.H * 128 * query_bytes(wl)
                    + wl.B * inp.max_pages * 4 + wl.B * 4 + rows * wl.topk * 4 + rows * wl.H * 128 * 2 + rows * wl.H * 4)
     reuse_gbps = reuse_bytes / (reuse_us * 1e-6) / 1e9
 
@@ -397,7 +408,8 @@ def main():
                         f"full decode_step ({'eager' if args.eager else 'HIP graph replay'})",
             "B": wl.B, "q": wl.q, "H": wl.H, "H_I": wl.H_I, "topk": wl.topk,
             "context": int(inp.contexts.max()), "cache_replicas": R,
-            "arithmetic": "bf16 MFMA for index scores, QK and PV (fp4 / e4m3 widened exactly to bf16), f32 accumulate",
+            "arithmetic": "bf16 MFMA for index scores, QK and PV (e2m1 codes times their block scale, e4m3 codes: "
+                          "widened exactly to bf16), f32 accumulate",
         },
         "hbm": {"algorithmic_bytes_per_step": ab["total"], "GBps": step_gbps, "peak_GBps": HBM_PEAK_GBPS,
                 "frac": step_gbps / HBM_PEAK_GBPS, "index_bytes": ab["index_pages"],

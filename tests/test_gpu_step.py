@@ -147,11 +147,12 @@ B32_SEQS = (0, 4, 9, 13, 17, 22, 26, 31)
 
 
 @pytest.mark.parametrize("name,b", [("headline", b) for b in range(4)] + [("long", b) for b in range(4)]
-                         + [("b32", b) for b in B32_SEQS])
+                         + [("b32", b) for b in B32_SEQS] + [("headline_nvfp4", b) for b in (0, 3)])
 def test_decode_step_full_size(mx, name, b):
     """The bench's workloads in the launch configuration it times: every
     sequence of the 256K and ragged 128K-256K steps, 8 of the 32 sequences of
-    the B = 32 step, each against the oracle's step for that sequence."""
+    the B = 32 step, 2 of the 4 sequences of the 256K step over NVFP4 caches,
+    each against the oracle's step for that sequence."""
     inp, g = cached_run(mx, name)
     check_step(inp, g, [b])
     if b == 0:

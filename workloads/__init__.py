@@ -23,6 +23,8 @@ Workloads (the shapes of the pages' decode configurations, one TP rank's share):
 - ``nvfp4``  B=4, q=8, 16:1, NVFP4 K/V and index (e2m1 in 16-element blocks,
              e4m3 block scales, per-token fp32 scale), context 16384 - u,
              top-k 16, 1 % outliers x20.
+- ``headline_nvfp4`` the headline shape (B=4, q=8, every context 262144,
+             top-k 32) over NVFP4 K/V and index caches, bf16 query.
 
 Values: K, V, index-K and q are N(0, 1) fp32; with ``outliers`` about 1 % of
 the elements (Binomial(N, 0.01) uniformly drawn positions) are multiplied by 20. Index queries are bf16 (fp32 N(0,1)
@@ -108,6 +110,8 @@ WORKLOADS = {
                     ("uniform", 8192, 262144)),
     "nvfp4": Workload("nvfp4", 6, 4, 8, 16, 4, 16, "nvfp4", "nvfp4", "bf16", True,
                       ("fixed_minus_u", 16384, 127)),
+    "headline_nvfp4": Workload("headline_nvfp4", 7, 4, 8, 16, 4, 32, "nvfp4", "nvfp4", "bf16", True,
+                               ("fixed", 262144)),
 }
 
 
