@@ -358,6 +358,23 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     reuse_us = ev0.elapsed_time(ev1) * 1e3 / (n_rep * R)
+    # the same step as one launch (decode_step_reuse_one_launch), timed the same way
+    reuse1 = [mx.DecodeStepReuse(c, t["query"], tb, wl.sm_scale, k_new=t.get("k_new"), v_new=t.get("v_new"),
+                                 one_launch=True) for c, tb in zip(caches, tables)]
+    for s_ in reuse1:
+        s_.run()
+    gr1 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr1):
+        for s_ in reuse1:
+            s_.run()
+    gr1.replay()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(n_rep):
+        gr1.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    reuse1_us = ev0.elapsed_time(ev1) * 1e3 / (n_rep * R)
     reuse_bytes = (ab["kv_pages"] + 2 * rows * 128 * 4 + 2 * rows * ROW_BYTES[wl.kv_format]
                    + rows * wl.H * 128 * query_bytes(wl)
                    + wl.B * inp.max_pages * 4 + wl.B * 4 + rows * wl.topk * 4 + rows * wl.H * 128 * 2 + rows * wl.H * 4)
@@ -437,13 +454,17 @@ def main():
         "us_per_step": reuse_us, "query_rows_per_s": rows / (reuse_us * 1e-6),
         "roofline": {"bound": "hbm", "achieved": reuse_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": reuse_gbps / HBM_PEAK_GBPS, "algorithmic_bytes_per_step": reuse_bytes},
+        "one_launch": {"what": "decode_step_reuse_one_launch: the same step as one launch (store workgroups, "
+                               "then attention workgroups that wait for their sequence's stores)",
+                       "us_per_step": reuse1_us, "query_rows_per_s": rows / (reuse1_us * 1e-6),
+                       "GBps": reuse_bytes / (reuse1_us * 1e-6) / 1e9},
     }
     if one_us is not None:
         out["one_launch_step"] = {"what": "decode_step_one_launch: the same step as one launch (scoring and attention "
                                           "workgroups in one grid), graph of R steps",
                                   "us_per_step": one_us, "query_rows_per_s": rows / (one_us * 1e-6),
                                   "GBps": ab["total"] / (one_us * 1e-6) / 1e9}
-    log(f"[bench] attention-only step {reuse_us:.1f} us = {reuse_gbps:.0f} GB/s")
+    log(f"[bench] attention-only step {reuse_us:.1f} us = {reuse_gbps:.0f} GB/s; as one launch {reuse1_us:.1f} us")
     if rep_us:
         log(f"[bench] per replay of {R} steps: median {rep_us[len(rep_us) // 2]:.1f} us per step "
             f"(p10 {rep_us[len(rep_us) // 10]:.1f}, p90 {rep_us[(9 * len(rep_us)) // 10]:.1f}; {len(rep_us)} replays)")

@@ -294,6 +294,27 @@ int mxs_workspace_init(void *ws, size_t ws_bytes, void *stream);
 int decode_step_reuse(const mxs_step *step, const int32_t *block_table, void *ws, size_t ws_bytes,
                       void *stream);
 
+/* decode_step_reuse_one_launch: decode_step_reuse as one launch (the same
+ * step as above, ATOM PR #2686). The grid holds one store workgroup per
+ * query row (its new K and V rows, device-coherent stores), then the
+ * attention workgroups of decode_step_reuse. With an MXFP4 KV cache each of
+ * them rounds the query to e4m3 in registers (the same codes pack_q_e4m3
+ * stores), and a wave whose token range holds one of the step's new positions
+ * waits (a bounded spin) until every store workgroup of its sequence has
+ * counted in, just before it requests those pages; the other waves never
+ * wait. Store workgroups have the lower ids and wait for nothing, and
+ * workgroups are dispatched in increasing id order, so no wait depends on a
+ * workgroup that cannot start. Output, lse and pages are bit for bit those of
+ * decode_step_reuse.
+ *   ws  as for decode_step_reuse, and zero before its first use
+ *       (mxs_workspace_init): its merge counters and two counter words per
+ *       sequence must start at zero; every call leaves them zero again (as
+ *       do decode_step, decode_step_reuse and decode_step_one_launch on the
+ *       same workspace), so a workspace is initialized once.
+ * Arguments and errors as for decode_step_reuse. */
+int decode_step_reuse_one_launch(const mxs_step *step, const int32_t *block_table, void *ws, size_t ws_bytes,
+                                 void *stream);
+
 /* decode_step_noalloc: decode_step for callers that cannot allocate device
  * memory (code under HIP graph capture that may not allocate, tight serving
  * loops, harnesses that forbid allocation). Same arguments, results, errors

@@ -26,7 +26,7 @@ EXPORTS = [
     "index_score_topk", "mxs_score_workspace_bytes", "sparse_split_attn", "mxs_default_partitions",
     "lse_merge", "decode_step", "decode_step_reuse", "mxs_workspace_bytes", "mxs_status_str", "mxs_last_error",
     "mxs_abi_version", "mxs_read_index_pages", "decode_step_noalloc", "mxs_workspace_init",
-    "decode_step_one_launch",
+    "decode_step_one_launch", "decode_step_reuse_one_launch",
 ]
 NOALLOC_SCRATCH_BYTES = 8 << 20        # MXS_NOALLOC_SCRATCH_BYTES
 
@@ -83,6 +83,7 @@ def lib() -> ctypes.CDLL:
             "lse_merge": [P, P, P, I32, I32, P, P, P],
             "decode_step": [P, P, SZ, P],
             "decode_step_reuse": [P, P, P, SZ, P],
+            "decode_step_reuse_one_launch": [P, P, P, SZ, P],
             "decode_step_noalloc": [P, P],
             "mxs_workspace_init": [P, SZ, P],
             "decode_step_one_launch": [P, P, SZ, P],
@@ -375,10 +376,12 @@ class DecodeStepReuse:
     """decode_step_reuse over fixed tensors: the step of a layer that reuses an
     earlier layer's block selection (``block_table`` [B][q][topk] int32). Stores
     the new K / V rows (both or neither), packs the query and attends over the
-    given blocks; the index side is not touched. ``run()`` is a single C call."""
+    given blocks; the index side is not touched. ``run()`` is a single C call.
+    ``one_launch``: decode_step_reuse_one_launch (one grid; the workspace must
+    be zero before its first use, which a workspace made here is)."""
 
     def __init__(self, cache: Cache, query, block_table, sm_scale, k_new=None, v_new=None, num_partitions=0,
-                 out=None, lse=None, ws=None):
+                 out=None, lse=None, ws=None, one_launch=False):
         B, q, H, _ = query.shape
         cache.check_batch(B)
         topk = block_table.shape[-1]
@@ -406,8 +409,9 @@ class DecodeStepReuse:
             _dev(self.out, torch.bfloat16, "out", (B, q, H, 128)), _opt(self.lse, torch.float32, "lse", (B, q, H)),
             None, None)
         self._ws_ptr = _dev(self.ws, torch.uint8, "ws")
+        self._fn = "decode_step_reuse_one_launch" if one_launch else "decode_step_reuse"
 
     def run(self, stream=None):
         s = _stream() if stream is None else stream
-        _check(lib().decode_step_reuse(ctypes.byref(self.struct), self._table, self._ws_ptr, self.ws.numel(), s))
+        _check(getattr(lib(), self._fn)(ctypes.byref(self.struct), self._table, self._ws_ptr, self.ws.numel(), s))
         return self.out

@@ -446,7 +446,11 @@ int decode_step_one_launch(const mxs_step *a, void *ws, size_t ws_bytes, void *s
   return step_entry(a, ws, ws_bytes, stream, true);
 }
 
-int decode_step_reuse(const mxs_step *a, const int32_t *block_table, void *ws, size_t ws_bytes, void *stream) {
+// The argument checks of decode_step_reuse (and of decode_step_reuse_one_launch),
+// then the launches of the one or the other.
+static int reuse_entry(const mxs_step *a, const int32_t *block_table, void *ws, size_t ws_bytes, void *stream,
+                       bool one_launch) {
+  const char *name = one_launch ? "decode_step_reuse_one_launch" : "decode_step_reuse";
   REQ(a, MXS_EINVAL, "step: null");
   const mxs_cache *cache = &a->cache;
   if (int r = check_cache(cache, false, true)) return r;
@@ -474,8 +478,8 @@ int decode_step_reuse(const mxs_step *a, const int32_t *block_table, void *ws, s
   REQ(a->out && aligned(a->out, 4), MXS_EINVAL, "out: null or misaligned");
   REQ(!a->lse || aligned(a->lse, 4), MXS_EINVAL, "lse: misaligned");
   const StepWs w = step_ws(a->B, a->q, a->H, a->topk, cache->page_table_stride, P);
-  REQ(ws, MXS_EWORKSPACE, "decode_step_reuse: workspace null (needs %zu bytes)", w.total);
-  REQ(ws_bytes >= w.total, MXS_EWORKSPACE, "decode_step_reuse: workspace %zu bytes, needs %zu", ws_bytes, w.total);
+  REQ(ws, MXS_EWORKSPACE, "%s: workspace null (needs %zu bytes)", name, w.total);
+  REQ(ws_bytes >= w.total, MXS_EWORKSPACE, "%s: workspace %zu bytes, needs %zu", name, ws_bytes, w.total);
   REQ(aligned(ws, 256), MXS_EINVAL, "ws: not 256-byte aligned");
 
   uint8_t *base = static_cast<uint8_t *>(ws);
@@ -484,8 +488,18 @@ int decode_step_reuse(const mxs_step *a, const int32_t *block_table, void *ws, s
   float *sp_l = reinterpret_cast<float *>(base + w.sp_l);
   float *sp_o = reinterpret_cast<float *>(base + w.sp_o);
   uint32_t *counters = reinterpret_cast<uint32_t *>(base + w.counters);
+  uint32_t *seq_cnt = reinterpret_cast<uint32_t *>(base + w.seq_cnt);
   const hipStream_t s = (hipStream_t)stream;
   const mxs::CacheView c = view(cache);
+  mxs::FusedMerge fm;
+  fm.counters = counters;
+  fm.out = a->out;
+  fm.lse = a->lse;
+
+  if (one_launch)   // store workgroups, then attention workgroups that wait for their sequence's stores
+    return launched(mxs::launch_reuse_step(c, a->k_new, a->v_new, a->query, a->q_dtype, block_table, a->B, a->q,
+                                           a->H, a->topk, P, a->sm_scale, sp_m, sp_l, sp_o, fm, seq_cnt, s),
+                    name);
 
   // 1 - 2: the new K / V rows into the pages, q -> e4m3 (MXFP4 KV) and the
   // merge counters cleared, one launch
@@ -495,13 +509,18 @@ int decode_step_reuse(const mxs_step *a, const int32_t *block_table, void *ws, s
     return r;
   // 5 - 6: split attention over the given blocks and the merge, one launch
   const void *qa = mx ? static_cast<const void *>(q8) : a->query;
-  mxs::FusedMerge fm;
-  fm.counters = counters;
-  fm.out = a->out;
-  fm.lse = a->lse;
   return launched(mxs::launch_table_attn(c, block_table, qa, a->B, a->q, a->H, a->topk, P, a->sm_scale, sp_m, sp_l,
                                          sp_o, fm, s),
                   "decode_step_reuse: split attention + merge");
+}
+
+int decode_step_reuse(const mxs_step *a, const int32_t *block_table, void *ws, size_t ws_bytes, void *stream) {
+  return reuse_entry(a, block_table, ws, ws_bytes, stream, false);
+}
+
+int decode_step_reuse_one_launch(const mxs_step *a, const int32_t *block_table, void *ws, size_t ws_bytes,
+                                 void *stream) {
+  return reuse_entry(a, block_table, ws, ws_bytes, stream, true);
 }
 
 }  // extern "C"

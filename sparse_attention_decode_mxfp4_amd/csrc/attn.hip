@@ -48,6 +48,7 @@
 #include "merge.hpp"
 #include "mxsparse.h"
 #include "score.hpp"
+#include "rowstore.hpp"
 
 namespace mxs {
 
@@ -176,6 +177,53 @@ __device__ __forceinline__ void load_query(const void *__restrict__ qv, int row,
       static_assert(!COH || FMT == 0, "the single-launch step packs an e4m3 query");
       q.c[s] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(qv) + base + 8 * s);
     }
+  }
+}
+
+// The lane's query elements as load_query takes them (head n, elements
+// 32 kg + 8 s .. + 7), from the caller's fp32 or bf16 query, for a launch that
+// rounds the query to e4m3 itself instead of reading packed codes.
+struct RawQuery {
+  u32x4 v[8];                                      // fp32: k-step s in v[2 s], v[2 s + 1]; bf16: in v[s]
+};
+__device__ __forceinline__ void load_query_raw(const void *__restrict__ qv, int q_dtype, int row, int H, int n, int kg,
+                                               RawQuery &r) {
+  const int64_t base = ((int64_t)row * H + (n < H ? n : 0)) * kDim + 32 * kg;
+  if (q_dtype == 1) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) r.v[s] = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(qv) + base + 8 * s);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r.v[k] = *reinterpret_cast<const u32x4 *>(static_cast<const float *>(qv) + base + 4 * k);
+  }
+}
+// Two values as e4m3 codes in bytes 0 and 1 (or 2 and 3, HI) of `old`: the
+// saturating e4m3 store's rounding. v_cvt_pk_fp8_f32 rounds to nearest even
+// and gives NaN above 464 (checked on MI355X against the software encoder on
+// every e4m3 midpoint, its neighbours and the range's ends), so values past
+// +-448 are first set to +-448; NaN fails the comparison and stays NaN.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b, uint32_t old) {
+  a = __builtin_fabsf(a) > 448.0f ? __builtin_copysignf(448.0f, a) : a;
+  b = __builtin_fabsf(b) > 448.0f ? __builtin_copysignf(448.0f, b) : b;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+}
+__device__ __forceinline__ void round_query_e4m3(const RawQuery &r, int q_dtype, QueryRegs<0> &q) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    float x[8];
+    if (q_dtype == 1) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[2 * k] = u2f(r.v[s][k] << 16);
+        x[2 * k + 1] = u2f(r.v[s][k] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = u2f(r.v[2 * s + (k >> 2)][k & 3]);
+    }
+    q.c[s].x = e4m3_pair<true>(x[2], x[3], e4m3_pair<false>(x[0], x[1], 0u));
+    q.c[s].y = e4m3_pair<true>(x[6], x[7], e4m3_pair<false>(x[4], x[5], 0u));
   }
 }
 
@@ -341,11 +389,15 @@ __device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t
 // the row's position is skipped (every range taken has a visible token). The
 // first range is peeled off the loop (a loop header would make its page
 // requests wait for every load still in flight, the query's included), and
-// partly masked ranges take their own code path.
-template <int FMT, int NW, int NT, class BlkOf, class PhysOf>
+// partly masked ranges take their own code path. gate(t_last) runs before a
+// range's pages are requested (t_last: the range's last position).
+struct NoGate {
+  __device__ void operator()(int) const {}
+};
+template <int FMT, int NW, int NT, class BlkOf, class PhysOf, class Gate = NoGate>
 __device__ __forceinline__ void attend_slots(const CacheView &c, int slot0, int slot1, int pos, const QueryRegs<FMT> &q,
                                              int H, float qk_scale2, float &m_run, float &l_run, f32x4 O[8], int n,
-                                             int kg, BlkOf blk_of, PhysOf phys_of) {
+                                             int kg, BlkOf blk_of, PhysOf phys_of, Gate gate = Gate{}) {
   constexpr int kRanges = 8 / NT, kSpan = 16 * NT, kSlotStep = NW / kRanges;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int toff = (wave % kRanges) * kSpan;
@@ -363,12 +415,14 @@ __device__ __forceinline__ void attend_slots(const CacheView &c, int slot0, int 
     return false;
   };
   if (!next()) return;
+  gate(t0 + kSpan - 1);
   if (t0 + kSpan - 1 <= pos)
     attend_block<FMT, true, true, NT>(c, phys, toff, t0, pos, q, H, qk_scale2, m_run, l_run, O, n, kg);
   else
     attend_block<FMT, false, true, NT>(c, phys, toff, t0, pos, q, H, qk_scale2, m_run, l_run, O, n, kg);
   slot += kSlotStep;
   while (next()) {
+    gate(t0 + kSpan - 1);
     if (t0 + kSpan - 1 <= pos)
       attend_block<FMT, true, false, NT>(c, phys, toff, t0, pos, q, H, qk_scale2, m_run, l_run, O, n, kg);
     else
@@ -565,6 +619,32 @@ struct StepWait {
 // a second): a bound that every wave reaches even if a count never arrives.
 constexpr uint32_t kWaitSpins = 1u << 21;
 
+// How an attention workgroup gets what other workgroups of the same launch
+// wrote. kTwoLaunch: nothing (the scores and e4m3 query come from an earlier
+// launch). kOneLaunchStep: the single-launch decode step — wait for the
+// sequence's scoring workgroups first, then read the scores and the e4m3 query
+// device-coherently. kOneLaunchReuse: the single-launch reuse step — the query
+// is rounded to e4m3 in registers from the caller's fp32 / bf16 query (MXFP4
+// K / V), and only a wave whose token range holds the step's new positions
+// waits, just before requesting those pages, for the sequence's store
+// workgroups.
+enum AttnMode { kTwoLaunch = 0, kOneLaunchStep = 1, kOneLaunchReuse = 2 };
+
+// The single-launch reuse step's bookkeeping of sequence b, run by the
+// workgroup that completes one of the sequence's rows (its merging workgroup,
+// or the only one when P = 1): the last of the q_rows takes the store count
+// seq_cnt[2 b] back by q_rows (a subtraction, so that a store workgroup's
+// count arriving after it still nets to zero when the launch ends) and clears
+// its own counter seq_cnt[2 b + 1]. Every wait of the sequence precedes its
+// workgroup's arrival and so precedes this.
+__device__ __forceinline__ void reuse_row_done(const StepWait &sw, int b, int q_rows) {
+  if (__hip_atomic_fetch_add(sw.seq_cnt + 2 * b + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+      (uint32_t)(q_rows - 1)) {
+    __hip_atomic_fetch_sub(sw.seq_cnt + 2 * b, (uint32_t)q_rows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(sw.seq_cnt + 2 * b + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // The decode step's attention workgroup (partition p of query row j of
 // sequence b). SELECT: the workgroup first selects its row's top-k blocks
 // itself (the workgroup selection of topk.hpp over the row's scores) and
@@ -574,18 +654,22 @@ constexpr uint32_t kWaitSpins = 1u << 21;
 // row's page table is staged in LDS. Everything the workgroup needs from
 // memory before the K / V pages — the context length, the score row or table
 // row and the page-table row — is requested in one round trip; the query goes
-// out with the first block's pages. With a StepWait (the single-launch step)
-// the score row and the query were written earlier in the same launch by
-// other workgroups: the workgroup waits for its sequence's count first and
-// reads them with device-coherent loads.
-template <int FMT, int ITEMS, bool SELECT, bool WAIT>
+// out with the first block's pages. MODE: see AttnMode. (In the single-launch
+// modes the K / V pages holding the step's new rows are read only after the
+// wait for their stores, so no stale copy of them can be in this XCD's L2: it
+// holds no line that was not fetched in this launch, and every wave that
+// reads those pages has waited first.) q_dtype: the caller's query dtype
+// (kOneLaunchReuse with MXFP4 K / V only).
+template <int FMT, int ITEMS, bool SELECT, int MODE>
 __device__ __forceinline__ void step_attn_wg(const CacheView &c, const float *__restrict__ scores,
                                              const void *__restrict__ qv, int32_t q_rows, int32_t H, int32_t topk,
                                              int32_t P, float sm_scale, int32_t *__restrict__ block_table,
                                              float *__restrict__ sp_m, float *__restrict__ sp_l,
                                              float *__restrict__ sp_o, const FusedMerge &fm, const StepWait &sw,
-                                             int p, int j, int b, StepAttnSmem<ITEMS, SELECT> &sm) {
+                                             int p, int j, int b, StepAttnSmem<ITEMS, SELECT> &sm, int q_dtype = 0) {
   constexpr int NT = 64 * kStepWaves;              // threads
+  constexpr bool RAWQ = MODE == kOneLaunchReuse && FMT == 0;
+  static_assert(MODE != kOneLaunchReuse || !SELECT, "the reuse step selects nothing");
   const int row = b * q_rows + j;
   const int tid = threadIdx.x, lane = tid & 63;
   const int n = lane & 15, kg = lane >> 4;
@@ -598,11 +682,13 @@ __device__ __forceinline__ void step_attn_wg(const CacheView &c, const float *__
 #pragma unroll
   for (int r = 0; r < ITEMS; ++r) {
     const int i = min(tid + NT * r, stride - 1);   // clamped: unconditional loads
-    if constexpr (SELECT && !WAIT) v[r] = scores[(int64_t)row * stride + i];
+    if constexpr (SELECT && MODE == kTwoLaunch) v[r] = scores[(int64_t)row * stride + i];
     pt[r] = c.page_table[(int64_t)b * stride + i];
   }
   if constexpr (!SELECT) given = block_table[(int64_t)row * topk + min(lane, topk - 1)];
-  if constexpr (WAIT) {
+  RawQuery raw;
+  if constexpr (RAWQ) load_query_raw(qv, q_dtype, row, H, n, kg, raw);
+  if constexpr (MODE == kOneLaunchStep) {
     // the sequence's scores, new K / V rows and e4m3 query are complete once
     // all its scoring workgroups have counted in
     if (tid == 0) {
@@ -618,10 +704,12 @@ __device__ __forceinline__ void step_attn_wg(const CacheView &c, const float *__
       }
     }
     __syncthreads();
+    if constexpr (SELECT) {
 #pragma unroll
-    for (int r = 0; r < ITEMS; ++r) {
-      const int i = min(tid + NT * r, stride - 1);
-      v[r] = __hip_atomic_load(scores + (int64_t)row * stride + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int r = 0; r < ITEMS; ++r) {
+        const int i = min(tid + NT * r, stride - 1);
+        v[r] = __hip_atomic_load(scores + (int64_t)row * stride + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
   const int pos = L - q_rows + j;
@@ -644,24 +732,44 @@ __device__ __forceinline__ void step_attn_wg(const CacheView &c, const float *__
   const int cps = (topk + P - 1) / P;
   const int slot0 = p * cps, slot1 = min(slot0 + cps, n_sel);
   QueryRegs<FMT> qr;                               // widened after the first block's pages are requested
-  load_query<FMT, WAIT>(qv, row, H, n, kg, qr);
+  if constexpr (RAWQ)
+    round_query_e4m3(raw, q_dtype, qr);
+  else
+    load_query<FMT, MODE == kOneLaunchStep && FMT == 0>(qv, row, H, n, kg, qr);   // e4m3 written in the same launch
   float m_run = -__builtin_inff(), l_run = 0.0f;
   f32x4 O[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  attend_slots<FMT, kStepWaves, kStepTiles>(
-      c, slot0, slot1, pos, qr, H, sm_scale * kLog2e, m_run, l_run, O, n, kg,
-      [&](int slot) {
-        const int blk = __builtin_amdgcn_readlane((int)sel, slot);
-        if constexpr (SELECT) return blk;          // a candidate: 0 <= blk, blk * 128 <= pos
-        return (blk < 0 || blk >= stride || blk * kTokens > pos) ? -1 : blk;
-      },
-      [&](int blk) {
-        const int phys = __builtin_amdgcn_readfirstlane(sm.s_pt[blk]);
-        return (phys < 0 || phys >= c.num_pages) ? -1 : phys;
-      });
+  auto blk_of = [&](int slot) {
+    const int blk = __builtin_amdgcn_readlane((int)sel, slot);
+    if constexpr (SELECT) return blk;              // a candidate: 0 <= blk, blk * 128 <= pos
+    return (blk < 0 || blk >= stride || blk * kTokens > pos) ? -1 : blk;
+  };
+  auto phys_of = [&](int blk) {
+    const int phys = __builtin_amdgcn_readfirstlane(sm.s_pt[blk]);
+    return (phys < 0 || phys >= c.num_pages) ? -1 : phys;
+  };
+  if constexpr (MODE == kOneLaunchReuse) {
+    // a range reaching the step's new positions (L - q_rows ..) waits for the
+    // sequence's store workgroups (bounded)
+    const int new0 = L - q_rows;
+    attend_slots<FMT, kStepWaves, kStepTiles>(
+        c, slot0, slot1, pos, qr, H, sm_scale * kLog2e, m_run, l_run, O, n, kg, blk_of, phys_of, [&](int t_last) {
+          if (t_last < new0) return;
+          uint32_t spins = 0;
+          while ((uint32_t)__builtin_amdgcn_readfirstlane((int)__hip_atomic_load(
+                     sw.seq_cnt + 2 * b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < sw.n_score &&
+                 ++spins < kWaitSpins)
+            __builtin_amdgcn_s_sleep(2);
+        });
+  } else {
+    attend_slots<FMT, kStepWaves, kStepTiles>(c, slot0, slot1, pos, qr, H, sm_scale * kLog2e, m_run, l_run, O, n, kg,
+                                              blk_of, phys_of);
+  }
   if (P == 1) {                                     // the row is this workgroup's alone: no exchange
     write_row<kStepWaves>(sm.s_m, sm.s_l, sm.s_o, m_run, l_run, O, row, H, fm.out, fm.lse);
+    if constexpr (MODE == kOneLaunchReuse)
+      if (tid == 0) reuse_row_done(sw, b, q_rows);
     return;
   }
   write_partial<true, kStepWaves>(sm.s_m, sm.s_l, sm.s_o, m_run, l_run, O, row, H, P, p, sp_m, sp_l, sp_o);
@@ -679,7 +787,10 @@ __device__ __forceinline__ void step_attn_wg(const CacheView &c, const float *__
                 (uint32_t)(P - 1);
   lds_barrier();
   if (!sm.s_last) return;
-  if (tid == 0) fm.counters[row] = 0u;            // every arrival is in: the row's counter is free for the next launch
+  if (tid == 0) {
+    fm.counters[row] = 0u;                        // every arrival is in: the row's counter is free for the next launch
+    if constexpr (MODE == kOneLaunchReuse) reuse_row_done(sw, b, q_rows);
+  }
   merge_row(sp_m, sp_l, sp_o, row, H, P, fm.out, fm.lse);
 }
 
@@ -691,8 +802,8 @@ __global__ __launch_bounds__(64 * kStepWaves) void k_select_attn(CacheView c, co
                                                      float *__restrict__ sp_l, float *__restrict__ sp_o,
                                                      FusedMerge fm) {
   __shared__ StepAttnSmem<ITEMS, SELECT> sm;
-  step_attn_wg<FMT, ITEMS, SELECT, false>(c, scores, qv, q_rows, H, topk, P, sm_scale, block_table, sp_m, sp_l, sp_o,
-                                          fm, StepWait{}, blockIdx.x, blockIdx.y, blockIdx.z, sm);
+  step_attn_wg<FMT, ITEMS, SELECT, kTwoLaunch>(c, scores, qv, q_rows, H, topk, P, sm_scale, block_table, sp_m, sp_l,
+                                               sp_o, fm, StepWait{}, blockIdx.x, blockIdx.y, blockIdx.z, sm);
 }
 
 // ---------------------------------------------------------------- the step as one launch
@@ -736,8 +847,73 @@ __global__ __launch_bounds__(64 * kStepWaves) void k_decode_step(
   }
   const int a = (int)blockIdx.x - n_score;
   const int p = a % P, j = (a / P) % q, b = a / (P * q);
-  step_attn_wg<0, ITEMS, true, true>(c, scores, st.q8, q, H, topk, P, sm_scale, block_table, sp_m, sp_l, sp_o, fm,
-                                     sw, p, j, b, *reinterpret_cast<StepAttnSmem<ITEMS, true> *>(lds));
+  step_attn_wg<0, ITEMS, true, kOneLaunchStep>(c, scores, st.q8, q, H, topk, P, sm_scale, block_table, sp_m, sp_l,
+                                               sp_o, fm, sw, p, j, b, *reinterpret_cast<StepAttnSmem<ITEMS, true> *>(lds));
+}
+
+// ---------------------------------------------------------------- the reuse step as one launch
+// The step of a layer that reuses a block selection in one grid: one store
+// workgroup per query row first (ids below B q_rows: the row's new K and V
+// rows, device-coherent; then it counts itself in for its sequence), then the
+// attention workgroups (partition, row, sequence) over the given table
+// (kOneLaunchReuse: the query rounded to e4m3 in registers for MXFP4 K / V;
+// only the ranges that hold the step's new positions wait for the sequence's
+// store workgroups). The store workgroups wait for nothing and are
+// dispatched first (increasing ids per XCD), so every wait ends; it is also
+// bounded (kWaitSpins). The merge counters and the sequence counters
+// (seq_cnt) must be zero before the first launch and are left zero.
+template <int FMT, int ITEMS>
+__global__ __launch_bounds__(64 * kStepWaves) void k_reuse_step(
+    CacheView c, const float *__restrict__ k_new, const float *__restrict__ v_new, const void *__restrict__ q_src,
+    int32_t q_dtype, int32_t q_rows, int32_t H, int32_t topk, int32_t P, float sm_scale,
+    const int32_t *__restrict__ block_table, float *__restrict__ sp_m, float *__restrict__ sp_l,
+    float *__restrict__ sp_o, FusedMerge fm, StepWait sw, int32_t n_store) {
+  __shared__ StepAttnSmem<ITEMS, false> sm;
+  if ((int)blockIdx.x < n_store) {
+    const int row = blockIdx.x;
+    reuse_store_wg<true>(c, k_new, v_new, nullptr, 0, H, nullptr, nullptr, q_rows, row);
+    // every store of this workgroup done, then one arrival for the sequence
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(sw.seq_cnt + 2 * (row / q_rows), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  const int a = (int)blockIdx.x - n_store;
+  const int p = a % P, j = (a / P) % q_rows, b = a / (P * q_rows);
+  step_attn_wg<FMT, ITEMS, false, kOneLaunchReuse>(c, nullptr, q_src, q_rows, H, topk, P, sm_scale,
+                                                   const_cast<int32_t *>(block_table), sp_m, sp_l, sp_o, fm, sw, p, j,
+                                                   b, sm, q_dtype);
+}
+
+hipError_t launch_reuse_step(const CacheView &c, const float *k_new, const float *v_new, const void *q, int q_dtype,
+                             const int32_t *block_table, int32_t B, int32_t q_rows, int32_t H, int32_t topk,
+                             int32_t P, float sm_scale, float *sp_m, float *sp_l, float *sp_o, const FusedMerge &fm,
+                             uint32_t *seq_cnt, hipStream_t s) {
+  if (B * q_rows == 0) return hipSuccess;
+  constexpr int NT = 64 * kStepWaves;
+  StepWait sw;
+  sw.seq_cnt = seq_cnt;
+  sw.n_score = (uint32_t)q_rows;                   // store workgroups per sequence
+  const int n_store = B * q_rows;
+  const dim3 grid((unsigned)(n_store + B * q_rows * P)), block(NT);
+#define MXS_REUSE(F, I)                                                                                         \
+  hipLaunchKernelGGL((k_reuse_step<F, I>), grid, block, 0, s, c, k_new, v_new, q, q_dtype, q_rows, H, topk, P,   \
+                     sm_scale, block_table, sp_m, sp_l, sp_o, fm, sw, n_store)
+#define MXS_REUSE_FMT(F)                            \
+  if (c.stride <= NT * 2) MXS_REUSE(F, 2);          \
+  else if (c.stride <= NT * 8) MXS_REUSE(F, 8);     \
+  else MXS_REUSE(F, 32)
+  if (c.kv_format == 0) {
+    MXS_REUSE_FMT(0);
+  } else if (c.kv_format == 1) {
+    MXS_REUSE_FMT(1);
+  } else {
+    MXS_REUSE_FMT(2);
+  }
+#undef MXS_REUSE_FMT
+#undef MXS_REUSE
+  return hipGetLastError();
 }
 
 bool decode_step_one_launch(const CacheView &c, int32_t B, int32_t q) {

@@ -84,6 +84,18 @@ hipError_t launch_decode_step(const CacheView &c, const uint16_t *q_idx, const f
                               float sm_scale, int32_t *block_table, float *sp_m, float *sp_l, float *sp_o,
                               const FusedMerge &fm, uint32_t *seq_cnt, hipStream_t s);
 
+// the step of a layer that reuses a block selection as one launch (attn.hip):
+// store workgroups (the new K / V rows, device-coherent) and then attention
+// workgroups over the given block table; the query (fp32 / bf16 per q_dtype)
+// is rounded to e4m3 in registers for an MXFP4 KV cache, and only the token
+// ranges holding the step's new rows wait for their sequence's stores. The
+// merge counters fm.counters [B][q_rows] and seq_cnt [B][2] zero on entry and
+// left zero.
+hipError_t launch_reuse_step(const CacheView &c, const float *k_new, const float *v_new, const void *q, int q_dtype,
+                             const int32_t *block_table, int32_t B, int32_t q_rows, int32_t H, int32_t topk,
+                             int32_t P, float sm_scale, float *sp_m, float *sp_l, float *sp_o, const FusedMerge &fm,
+                             uint32_t *seq_cnt, hipStream_t s);
+
 // streaming read of every index page in page-table order (read.hip): a
 // measurement of the scan's bandwidth ceiling; sink receives at most one word
 hipError_t launch_read_pages(const CacheView &c, int32_t B, uint32_t page_bytes, uint32_t *sink, hipStream_t s);

@@ -14,6 +14,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace mxs {
 
@@ -162,6 +163,74 @@ __device__ __forceinline__ void pack_q4(const void *q, int q_dtype, int64_t n, u
         e4m3_code(v[0]) | (e4m3_code(v[1]) << 8) | (e4m3_code(v[2]) << 16) | (e4m3_code(v[3]) << 24);
   } else {
     for (int e = 0; e < m; ++e) q8[i + e] = (uint8_t)e4m3_code(v[e]);
+  }
+}
+
+// The stores of a step that reuses an earlier layer's block selection (the
+// pages' index_topk_freq schedule: such a layer scores nothing), one
+// workgroup per query row (row = b q_rows + j). The workgroup stores the new
+// K and V rows of position L_b - q + j (wave 0: K, wave 1: V; skipped when
+// that position has no valid page), packs the row's H x 128 query elements
+// to e4m3 (waves 2 - 3, when q8 is given) and clears the row's merge counter
+// (when counters is given) for the attention that follows. Every load
+// that does not depend on another is requested before any result is used:
+// the source row goes out with the context length (the page id needs the
+// length), and each packing thread requests its 16 query elements at once.
+// COH: every store device-coherent (read by other workgroups of the same
+// launch once the workgroup has counted itself in).
+template <bool COH>
+__device__ __forceinline__ void reuse_store_wg(const CacheView &c, const float *__restrict__ k_new,
+                                               const float *__restrict__ v_new, const void *__restrict__ q,
+                                               int q_dtype, int H, uint8_t *__restrict__ q8,
+                                               uint32_t *__restrict__ counters, int q_rows, int row) {
+  const int b = row / q_rows, j = row % q_rows;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (counters && tid == 0) st_u32<COH>(counters + row, 0u);
+  if (wave < 2) {
+    const float *src = wave == 0 ? k_new : v_new;
+    if (!src) return;
+    const float2 x = reinterpret_cast<const float2 *>(src + (int64_t)row * kDim)[lane];
+    const int pos = c.context_lens[b] - q_rows + j;
+    if (pos < 0 || pos / kTokens >= c.stride) return;
+    const int phys = c.page_table[(int64_t)b * c.stride + pos / kTokens];
+    if (phys < 0 || phys >= c.num_pages) return;
+    store_row<COH>(c.kv_format, x, wave == 0 ? c.k_pages : c.v_pages, phys, pos % kTokens, lane);
+  } else if (q8) {
+    // elements e0 .. e0 + 15 of the row (H x 128 <= 2048 = 16 x 128 threads);
+    // the query is 16-byte aligned, so are the row and each thread's run
+    const int t = tid - 128;
+    if (16 * t >= H * kDim) return;
+    const int64_t e0 = (int64_t)row * H * kDim + 16 * t;
+    float v[16];
+    if (q_dtype == 1) {                               // bf16: element 2k in the low half of dword k
+      const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(q) + e0);
+      const u32x4 a0 = p[0], a1 = p[1];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] = u2f(a0[k] << 16);
+        v[2 * k + 1] = u2f(a0[k] & 0xFFFF0000u);
+        v[8 + 2 * k] = u2f(a1[k] << 16);
+        v[8 + 2 * k + 1] = u2f(a1[k] & 0xFFFF0000u);
+      }
+    } else {
+      const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const float *>(q) + e0);
+      u32x4 a[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) a[k] = p[k];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = u2f(a[k >> 2][k & 3]);
+    }
+    u32x4 codes;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      codes[k] = e4m3_code(v[4 * k]) | (e4m3_code(v[4 * k + 1]) << 8) | (e4m3_code(v[4 * k + 2]) << 16) |
+                 (e4m3_code(v[4 * k + 3]) << 24);
+    if constexpr (COH) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) st_u32<true>(reinterpret_cast<uint32_t *>(q8 + e0) + k, codes[k]);
+    } else {
+      *reinterpret_cast<u32x4 *>(q8 + e0) = codes;      // q8: the step workspace, 16-byte aligned
+    }
   }
 }
 

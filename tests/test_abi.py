@@ -31,7 +31,7 @@ def test_header_declares_the_stages():
               "index_score_topk", "sparse_split_attn", "lse_merge", "decode_step", "decode_step_reuse",
               "mxs_workspace_bytes",
               "mxs_default_partitions", "mxs_status_str", "mxs_last_error", "mxs_abi_version",
-              "mxs_score_workspace_bytes", "decode_step_noalloc"]:
+              "mxs_score_workspace_bytes", "decode_step_noalloc", "decode_step_reuse_one_launch"]:
         assert f in names, f
     assert set(names) == set(mx.EXPORTS)
 
@@ -160,6 +160,26 @@ def test_decode_step_reuse_rejects_before_launch(L):
     s.q_dtype = mx.MXS_F32
     s.B = 0                           # an empty batch does nothing and succeeds
     assert L.decode_step_reuse(P(s), table, None, 0, None) == mx.MXS_OK
+
+
+def test_decode_step_reuse_one_launch_rejects_like_the_two_launch_step(L):
+    """The one-launch reuse step shares the two-launch step's argument checks
+    (and names itself in the messages)."""
+    P = ctypes.byref
+    s = mx.StepStruct(_cache(idx_pages=0), 0, 0, 0, 4096, mx.MXS_F32, 0, 0, 2, 8, 16, 0, 32, 0, 0.1, 16384, 0, 0, 0)
+    need = L.mxs_workspace_bytes(2, 8, 16, 1, 32, 16, 0)
+    ws, table = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 16)
+    assert L.decode_step_reuse_one_launch(P(s), None, ws, need, None) == mx.MXS_EINVAL
+    assert L.decode_step_reuse_one_launch(P(s), table, ws, need - 1, None) == mx.MXS_EWORKSPACE
+    assert "decode_step_reuse_one_launch" in _err(L)
+    s.k_new = 4096
+    assert L.decode_step_reuse_one_launch(P(s), table, ws, need, None) == mx.MXS_EINVAL
+    s.k_new = 0
+    s.q_dtype = mx.MXS_E4M3
+    assert L.decode_step_reuse_one_launch(P(s), table, ws, need, None) == mx.MXS_EUNSUPPORTED
+    s.q_dtype = mx.MXS_F32
+    s.B = 0
+    assert L.decode_step_reuse_one_launch(P(s), table, None, 0, None) == mx.MXS_OK
 
 
 def test_read_index_pages_rejects_before_launch(L):

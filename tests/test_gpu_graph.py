@@ -70,7 +70,8 @@ def test_decode_step_graph_replays_equal_eager(mx, name):
     PT.check_attention(out0.float().cpu().numpy()[0], r["O"][0], f"{name} graph b=0")
 
 
-def test_reuse_step_graph_replays_equal_eager(mx):
+@pytest.mark.parametrize("one_launch", [False, True])
+def test_reuse_step_graph_replays_equal_eager(mx, one_launch):
     inp, cache, t = _setup("mxfp4_65k")
     wl = inp.wl
     full = mx.DecodeStep(cache, t["query"], t["q_idx"], t["w"], wl.topk, wl.sm_scale, k_new=t.get("k_new"),
@@ -79,7 +80,8 @@ def test_reuse_step_graph_replays_equal_eager(mx):
     full.run()
     torch.cuda.synchronize()
     table = full.block_table_out.clone()
-    step = mx.DecodeStepReuse(cache, t["query"], table, wl.sm_scale, k_new=t.get("k_new"), v_new=t.get("v_new"))
+    step = mx.DecodeStepReuse(cache, t["query"], table, wl.sm_scale, k_new=t.get("k_new"), v_new=t.get("v_new"),
+                              one_launch=one_launch)
     step.run()
     torch.cuda.synchronize()
     out0, lse0 = step.out.clone(), step.lse.clone()

@@ -45,7 +45,7 @@ def random_table(inp, seed):
     return t
 
 
-def run_reuse(mx, inp, table, num_partitions=0, store=True):
+def run_reuse(mx, inp, table, num_partitions=0, store=True, one_launch=False):
     import workloads.gpu as WG
     wl = inp.wl
     pools = WG.fill_prefix(inp, WG.empty_pools(inp))
@@ -54,7 +54,8 @@ def run_reuse(mx, inp, table, num_partitions=0, store=True):
     t = WG.step_tensors(inp)
     tab = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).cuda()
     step = mx.DecodeStepReuse(cache, t["query"], tab, wl.sm_scale, k_new=t.get("k_new") if store else None,
-                              v_new=t.get("v_new") if store else None, num_partitions=num_partitions)
+                              v_new=t.get("v_new") if store else None, num_partitions=num_partitions,
+                              one_launch=one_launch)
     step.run()
     torch.cuda.synchronize()
     assert torch.equal(pools["idx"], idx_before), "the index pool changed"
@@ -77,12 +78,58 @@ def check_reuse(inp, g, table, seqs):
         assert (np.isneginf(g["lse"][b]) == np.isneginf(r["lse"][b])).all()
 
 
+@pytest.mark.parametrize("one_launch", [False, True])
 @pytest.mark.parametrize("name", ["tiny", "fp8", "mxfp4_65k", "nvfp4"])
-def test_reuse_step_small(mx, name):
+def test_reuse_step_small(mx, name, one_launch):
     inp = W.make_inputs(W.WORKLOADS[name])
     table = random_table(inp, 11)
-    g = run_reuse(mx, inp, table)
+    g = run_reuse(mx, inp, table, one_launch=one_launch)
     check_reuse(inp, g, table, range(inp.wl.B))
+
+
+# decode_step_reuse_one_launch against decode_step_reuse on every path the
+# two-launch tests cover: (workload overrides, table kind, partitions, row store)
+ONE_LAUNCH_CASES = [
+    ("mxfp4_65k", {}, "random", 0, True),
+    ("mxfp4_65k", dict(B=2), "random", 1, True),                  # P = 1: the row written without an exchange
+    ("mxfp4_65k", dict(B=2), "random", 64, True),                 # empty partitions
+    ("mxfp4_65k", dict(B=2), "noisy", 0, True),                   # entries < 0, past the table, past the position
+    ("mxfp4_65k", dict(B=2, full_step=False), "random", 0, False),   # no row store
+    ("tiny", dict(q=2), "empty", 0, True),                        # every slot -1
+    ("mxfp4_65k", dict(name="edge", ctx_rule=("list", (9, 130, 1000, 4096)), B=4, q=8, H=16, topk=16), "random", 0,
+     True),
+    ("mxfp4_65k", dict(name="edge", ctx_rule=("list", (5000, 3000)), B=2, q=16, H=7, H_I=3, topk=5), "random", 0,
+     True),
+    ("mxfp4_65k", dict(q_dtype="bf16"), "random", 0, True),       # bf16 source of the e4m3 query
+    ("fp8", {}, "random", 0, True),
+    ("nvfp4", {}, "random", 0, True),
+    ("long", dict(B=2), "random", 0, True),                       # 128K-256K contexts
+]
+
+
+@pytest.mark.parametrize("case", range(len(ONE_LAUNCH_CASES)))
+def test_reuse_one_launch_equals_two_launches(mx, case):
+    """decode_step_reuse_one_launch gives the output, lse and K / V pages of
+    decode_step_reuse bit for bit, and is checked against the oracle too."""
+    name, kw, kind, P, store = ONE_LAUNCH_CASES[case]
+    inp = W.make_inputs(W.WORKLOADS[name].with_(**kw) if kw else W.WORKLOADS[name])
+    wl = inp.wl
+    table = random_table(inp, 7)
+    if kind == "noisy":
+        table[:, :, 1] = -3
+        table[0, :, 2] = inp.max_pages + 7
+        table[1, :, 2] = 2 ** 30
+    elif kind == "empty":
+        table[:] = -1
+    two = run_reuse(mx, inp, table, num_partitions=P, store=store)
+    one = run_reuse(mx, inp, table, num_partitions=P, store=store, one_launch=True)
+    assert np.array_equal(one["O"], two["O"]) and np.array_equal(one["lse"], two["lse"])
+    for s in ("k", "v"):
+        assert np.array_equal(one["pools"][s], two["pools"][s]), s
+    if kind == "empty":                           # nothing attended: O = 0, lse = -inf (the oracle's row is 0 / 0)
+        assert (one["O"] == 0).all() and np.isneginf(one["lse"]).all()
+    else:
+        check_reuse(inp, one, table, range(wl.B) if name != "long" else [0])
 
 
 @pytest.mark.parametrize("name", ["tiny", "fp8", "mxfp4_65k", "nvfp4", "one_launch"])
@@ -165,9 +212,11 @@ def test_reuse_step_empty_table(mx):
     assert (g["O"] == 0).all() and np.isneginf(g["lse"]).all()
 
 
-def test_reuse_step_alternating_tables_share_a_workspace(mx):
+@pytest.mark.parametrize("one_launch", [False, True])
+def test_reuse_step_alternating_tables_share_a_workspace(mx, one_launch):
     """Two reuse steps over different tables alternate on one workspace: every
-    run equals its own first run bit for bit."""
+    run equals its own first run bit for bit (the single launch's counters
+    reset themselves between runs)."""
     import workloads.gpu as WG
     inp = W.make_inputs(W.WORKLOADS["mxfp4_65k"])
     wl = inp.wl
@@ -178,7 +227,7 @@ def test_reuse_step_alternating_tables_share_a_workspace(mx):
     ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
     tabs = [torch.from_numpy(random_table(inp, s).astype(np.int32)).cuda() for s in (1, 2)]
     steps = [mx.DecodeStepReuse(cache, t["query"], tb, wl.sm_scale, k_new=t.get("k_new"), v_new=t.get("v_new"),
-                                ws=ws) for tb in tabs]
+                                ws=ws, one_launch=one_launch) for tb in tabs]
     first = []
     for s_ in steps:
         s_.run()
