@@ -127,10 +127,10 @@ StepWs step_ws(int32_t B, int32_t q, int32_t H, int32_t topk, int32_t stride, in
   w.scores = off; off += round_up(rows * stride * sizeof(float));
   w.table = off;  off += round_up(rows * topk * sizeof(int32_t));
   w.q8 = off;     off += round_up(rows * H * MXS_HEAD_DIM);
-  w.sp_m = off;   off += round_up(rows * H * P * sizeof(float));
-  w.sp_l = off;   off += round_up(rows * H * P * sizeof(float));
+  w.sp_m = off;   off += round_up(rows * mxs::step_ml_stride(H, P) * sizeof(float));
+  w.sp_l = off;   off += round_up(rows * mxs::step_ml_stride(H, P) * sizeof(float));
   w.sp_o = off;   off += round_up(rows * H * P * MXS_HEAD_DIM * sizeof(float));
-  w.counters = off; off += round_up(rows * sizeof(uint32_t));
+  w.counters = off; off += round_up(rows * sizeof(uint64_t));
   w.seq_cnt = off;  off += round_up((size_t)B * 2 * sizeof(uint32_t));
   w.total = off;
   return w;
@@ -376,7 +376,7 @@ static int step_entry(const mxs_step *a, void *ws, size_t ws_bytes, void *stream
   float *sp_m = reinterpret_cast<float *>(base + w.sp_m);
   float *sp_l = reinterpret_cast<float *>(base + w.sp_l);
   float *sp_o = reinterpret_cast<float *>(base + w.sp_o);
-  uint32_t *counters = reinterpret_cast<uint32_t *>(base + w.counters);
+  uint64_t *counters = reinterpret_cast<uint64_t *>(base + w.counters);
   uint32_t *seq_cnt = reinterpret_cast<uint32_t *>(base + w.seq_cnt);
   const hipStream_t s = (hipStream_t)stream;
   const mxs::CacheView c = view(cache);
@@ -487,7 +487,7 @@ static int reuse_entry(const mxs_step *a, const int32_t *block_table, void *ws, 
   float *sp_m = reinterpret_cast<float *>(base + w.sp_m);
   float *sp_l = reinterpret_cast<float *>(base + w.sp_l);
   float *sp_o = reinterpret_cast<float *>(base + w.sp_o);
-  uint32_t *counters = reinterpret_cast<uint32_t *>(base + w.counters);
+  uint64_t *counters = reinterpret_cast<uint64_t *>(base + w.counters);
   uint32_t *seq_cnt = reinterpret_cast<uint32_t *>(base + w.seq_cnt);
   const hipStream_t s = (hipStream_t)stream;
   const mxs::CacheView c = view(cache);

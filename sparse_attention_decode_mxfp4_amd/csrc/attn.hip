@@ -492,7 +492,8 @@ __device__ __forceinline__ f32x4 merged(const float (&s_m)[NW][16], const float 
 template <bool COHERENT, int NW>
 __device__ __forceinline__ void write_partial(float (&s_m)[NW][16], float (&s_l)[NW][16],
                                               float (&s_o)[NW][16][kDim + 4], float m_run, float l_run,
-                                              const f32x4 O[8], int row, int H, int P, int p, float *__restrict__ sp_m,
+                                              const f32x4 O[8], int row, int H, int P, int p, int mls,
+                                              float *__restrict__ sp_m,
                                               float *__restrict__ sp_l, float *__restrict__ sp_o) {
   const float NEG_INF = -__builtin_inff();
   stage_waves<NW>(s_m, s_l, s_o, m_run, l_run, O);
@@ -522,8 +523,8 @@ __device__ __forceinline__ void write_partial(float (&s_m)[NW][16], float (&s_l)
 #pragma unroll
     for (int w = 0; w < NW; ++w)
       Lsum += (s_m[w][h] == NEG_INF) ? 0.0f : s_l[w][h] * __builtin_amdgcn_exp2f(s_m[w][h] - M);
-    put<COHERENT>(sp_m + (part + h) * P + p, M * kLn2);
-    put<COHERENT>(sp_l + (part + h) * P + p, Lsum);
+    put<COHERENT>(sp_m + (int64_t)row * mls + h * P + p, M * kLn2);
+    put<COHERENT>(sp_l + (int64_t)row * mls + h * P + p, Lsum);
   }
 }
 
@@ -592,7 +593,7 @@ __global__ __launch_bounds__(256) void k_split_attn(CacheView c, const void *__r
         const int phys = __builtin_amdgcn_readfirstlane(c.page_table[(int64_t)b * c.stride + blk]);
         return (phys < 0 || phys >= c.num_pages) ? -1 : phys;
       });
-  write_partial<false, kAttnWaves>(s_m, s_l, s_o, m_run, l_run, O, row, H, P, p, sp_m, sp_l, sp_o);
+  write_partial<false, kAttnWaves>(s_m, s_l, s_o, m_run, l_run, O, row, H, P, p, H * P, sp_m, sp_l, sp_o);
 }
 
 // Shared memory of one decode-step attention workgroup.
@@ -602,7 +603,7 @@ struct StepAttnSmem {
   int32_t s_pt[64 * kStepWaves * ITEMS];
   float s_m[kStepWaves][16], s_l[kStepWaves][16];
   float s_o[kStepWaves][16][kDim + 4];
-  uint32_t s_last;
+  uint32_t s_last, s_local;                        // merging workgroup; all arrivals on its XCC
 };
 
 // What the attention workgroups of the single-launch decode step wait for:
@@ -772,26 +773,52 @@ __device__ __forceinline__ void step_attn_wg(const CacheView &c, const float *__
       if (tid == 0) reuse_row_done(sw, b, q_rows);
     return;
   }
-  write_partial<true, kStepWaves>(sm.s_m, sm.s_l, sm.s_o, m_run, l_run, O, row, H, P, p, sp_m, sp_l, sp_o);
+  const int mls = step_ml_stride(H, P);
+  write_partial<true, kStepWaves>(sm.s_m, sm.s_l, sm.s_o, m_run, l_run, O, row, H, P, p, mls, sp_m, sp_l, sp_o);
 
   // ---- the row's merge, by its last partition workgroup to finish. The
   // partials went out as agent-scope (device-coherent) stores; once every
   // wave's stores are done (vmcnt) and the workgroup has met, one arrival is
-  // counted (device-scope atomic). The workgroup that takes the count to P
-  // reads every partition's partials with agent-scope loads. No cache
+  // counted (device-scope atomic): 1 in bits 0-7 and 1 in the 7-bit field of
+  // the workgroup's XCC (bits 8 + 7 x; P <= 64 keeps both from overflowing).
+  // The workgroup that takes the count to P reads every partition's partials:
+  // through its XCD's L2 when all P arrivals came from its own XCC (the
+  // placement of xcd_item makes that the usual case), with agent-scope loads
+  // otherwise. Plain loads are safe then: the partials reached that L2 (or
+  // memory) before their arrivals were counted, and this CU's L1 holds no
+  // line of them (L1 starts empty in a launch, only a row's merger reads its
+  // partials, and rows do not share lines: step_ml_stride). No cache
   // write-back or invalidate is needed on either side.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();
-  if (tid == 0)
-    sm.s_last = __hip_atomic_fetch_add(fm.counters + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                (uint32_t)(P - 1);
+  if (tid == 0) {
+    const uint32_t x = xcc_id();
+    const uint64_t inc = 1ull + (1ull << (8 + 7 * x));
+    const uint64_t old = __hip_atomic_fetch_add(fm.counters + row, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.s_last = (uint32_t)(old & 0xFFu) == (uint32_t)(P - 1);
+    sm.s_local = (uint32_t)(((old + inc) >> (8 + 7 * x)) & 0x7Fu) == (uint32_t)P;
+  }
   lds_barrier();
   if (!sm.s_last) return;
   if (tid == 0) {
-    fm.counters[row] = 0u;                        // every arrival is in: the row's counter is free for the next launch
+    fm.counters[row] = 0ull;                      // every arrival is in: the row's counter is free for the next launch
     if constexpr (MODE == kOneLaunchReuse) reuse_row_done(sw, b, q_rows);
   }
-  merge_row(sp_m, sp_l, sp_o, row, H, P, fm.out, fm.lse);
+  if (sm.s_local)
+    merge_row<false>(sp_m, sp_l, sp_o, row, H, P, mls, fm.out, fm.lse);
+  else
+    merge_row<true>(sp_m, sp_l, sp_o, row, H, P, mls, fm.out, fm.lse);
+}
+
+// Work item of attention workgroup `lin` of a grid of n: workgroups are
+// dispatched to the 8 XCDs round robin by id (XCD = id % 8, checked on
+// MI355X with the hardware XCC id register), so when n is a multiple of 8
+// the items are dealt so that each XCD takes a run of consecutive items: a
+// row's partitions, and the rows of one sequence, share one XCD and its L2
+// (the score and page-table rows, the K / V pages the rows have in common).
+// Results do not depend on it.
+__device__ __forceinline__ int xcd_item(int lin, int n) {
+  return (n & 7) == 0 ? (lin & 7) * (n >> 3) + (lin >> 3) : lin;
 }
 
 template <int FMT, int ITEMS, bool SELECT>
@@ -802,8 +829,9 @@ __global__ __launch_bounds__(64 * kStepWaves) void k_select_attn(CacheView c, co
                                                      float *__restrict__ sp_l, float *__restrict__ sp_o,
                                                      FusedMerge fm) {
   __shared__ StepAttnSmem<ITEMS, SELECT> sm;
+  const int r = xcd_item(blockIdx.x, gridDim.x);   // item r: partition r % P, row (r / P) % q_rows, sequence
   step_attn_wg<FMT, ITEMS, SELECT, kTwoLaunch>(c, scores, qv, q_rows, H, topk, P, sm_scale, block_table, sp_m, sp_l,
-                                               sp_o, fm, StepWait{}, blockIdx.x, blockIdx.y, blockIdx.z, sm);
+                                               sp_o, fm, StepWait{}, r % P, (r / P) % q_rows, r / (P * q_rows), sm);
 }
 
 // ---------------------------------------------------------------- the step as one launch
@@ -845,7 +873,7 @@ __global__ __launch_bounds__(64 * kStepWaves) void k_decode_step(
     if (threadIdx.x == 0) __hip_atomic_fetch_add(sw.seq_cnt + 2 * b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  const int a = (int)blockIdx.x - n_score;
+  const int a = xcd_item((int)blockIdx.x - n_score, (int)gridDim.x - n_score);   // XCD runs when 8 divides n_score
   const int p = a % P, j = (a / P) % q, b = a / (P * q);
   step_attn_wg<0, ITEMS, true, kOneLaunchStep>(c, scores, st.q8, q, H, topk, P, sm_scale, block_table, sp_m, sp_l,
                                                sp_o, fm, sw, p, j, b, *reinterpret_cast<StepAttnSmem<ITEMS, true> *>(lds));
@@ -879,7 +907,7 @@ __global__ __launch_bounds__(64 * kStepWaves) void k_reuse_step(
       __hip_atomic_fetch_add(sw.seq_cnt + 2 * (row / q_rows), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  const int a = (int)blockIdx.x - n_store;
+  const int a = xcd_item((int)blockIdx.x - n_store, (int)gridDim.x - n_store);
   const int p = a % P, j = (a / P) % q_rows, b = a / (P * q_rows);
   step_attn_wg<FMT, ITEMS, false, kOneLaunchReuse>(c, nullptr, q_src, q_rows, H, topk, P, sm_scale,
                                                    const_cast<int32_t *>(block_table), sp_m, sp_l, sp_o, fm, sw, p, j,
@@ -977,7 +1005,7 @@ static void launch_attn_items(const CacheView &c, const float *scores, const voi
                               int32_t H, int32_t topk, int32_t P, float sm_scale, int32_t *block_table, float *sp_m,
                               float *sp_l, float *sp_o, const FusedMerge &fm, hipStream_t s) {
   constexpr int NT = 64 * kStepWaves;
-  const dim3 grid((unsigned)P, (unsigned)q_rows, (unsigned)B), block(NT);
+  const dim3 grid((unsigned)(P * q_rows * B)), block(NT);
 #define MXS_SELECT_ATTN(F, I)                                                                                   \
   hipLaunchKernelGGL((k_select_attn<F, I, SELECT>), grid, block, 0, s, c, scores, q, q_rows, H, topk, P,       \
                      sm_scale, block_table, sp_m, sp_l, sp_o, fm)

@@ -168,11 +168,26 @@ __device__ __forceinline__ void st_u32(uint32_t *p, uint32_t v) {
     *p = v;
 }
 template <bool COH>
+__device__ __forceinline__ void st_u64(uint64_t *p, uint64_t v) {
+  if constexpr (COH)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+template <bool COH>
 __device__ __forceinline__ void st_f32(float *p, float v) {
   if constexpr (COH)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   else
     *p = v;
+}
+
+// The XCC (one of the 8 accelerator dies, each with its own L2) this wave
+// runs on: the low 3 bits of the hardware register XCC_ID.
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  return x & 7u;
 }
 
 // ---------------------------------------------------------------- wave helpers

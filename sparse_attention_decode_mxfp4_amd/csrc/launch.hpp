@@ -15,6 +15,11 @@ struct CacheView {
   const int32_t *context_lens;
 };
 
+// Floats per query row of the decode step's partial maxima and sums (sp_m,
+// sp_l [rows][stride], head h of partition p at h P + p): H P rounded up to
+// 32, so that no two rows share a 128-byte line.
+inline __host__ __device__ int step_ml_stride(int H, int P) { return (H * P + 31) & ~31; }
+
 // n words at p set to zero (store.hip)
 hipError_t launch_zero(uint32_t *p, size_t n, hipStream_t s);
 
@@ -26,7 +31,7 @@ hipError_t launch_pack_q(const void *q, int q_dtype, int64_t n, uint8_t *q8, hip
 // [B][q][128] fp32 (row j of sequence b at position L_b - q + j; either null:
 // none), the query packed to e4m3 when q8 is non-null, counters [B][q] cleared
 hipError_t launch_reuse_store(const CacheView &c, const float *k_new, const float *v_new, const void *q, int q_dtype,
-                              int32_t H, uint8_t *q8, uint32_t *counters, int32_t B, int32_t q_rows, hipStream_t s);
+                              int32_t H, uint8_t *q8, uint64_t *counters, int32_t B, int32_t q_rows, hipStream_t s);
 
 // The decode step's own stores, done inside the scorer launch (all null: none):
 // the new K / V / index rows [B][q][128] fp32 (row j of sequence b goes to
@@ -36,7 +41,7 @@ struct StepStore {
   const void *q_att = nullptr;
   int q_dtype = 0, H = 0;
   uint8_t *q8 = nullptr;
-  uint32_t *counters = nullptr;      // [B][q] cleared (the attention launch's merge counters)
+  uint64_t *counters = nullptr;      // [B][q] cleared (the attention launch's merge counters)
 };
 
 // index scores (score.hip)
@@ -59,7 +64,7 @@ hipError_t launch_split_attn(const CacheView &c, const void *q, int q_dtype,
 // last partition to finish merges the row into out / lse (counters [B][q_rows]
 // zero on entry; the merging workgroup sets its row's counter back to zero)
 struct FusedMerge {
-  uint32_t *counters = nullptr;
+  uint64_t *counters = nullptr;       // [B][q_rows]: arrivals (bits 0-7) and per-XCC arrivals (7 bits each from bit 8)
   uint16_t *out = nullptr;
   float *lse = nullptr;
 };

@@ -5,7 +5,8 @@
 //   lse = M + ln L.  Empty partitions (m_p = -inf) weigh nothing.
 // merge_one: one (query row, head) per wave (the stand-alone merge kernel);
 // lane p < P reads partition p's (m, l), each lane owns two output elements.
-// merge_row: one query row per workgroup (the decode step's in-launch merge).
+// merge_row: one query row per workgroup (the decode step's in-launch merge;
+// COH: the partials are read device-coherently, else through this XCD's L2).
 #pragma once
 
 #include "common.hpp"
@@ -26,6 +27,18 @@ __device__ __forceinline__ f32x4 load4_coherent(__amdgpu_buffer_rsrc_t rs, int32
 }
 __device__ __forceinline__ float load1_coherent(__amdgpu_buffer_rsrc_t rs, int32_t float_off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, float_off * 4, 0, kCoherentBits));
+}
+// Loads of another workgroup's partials: device-coherent (COH, sc1: past
+// this XCD's L2, for data written on any XCD) or plain (through this XCD's L2:
+// for data written on the same XCD, never loaded into this CU's L1 before).
+template <bool COH>
+__device__ __forceinline__ f32x4 load4_partial(__amdgpu_buffer_rsrc_t rs, int32_t float_off) {
+  return __builtin_bit_cast(f32x4,
+                            __builtin_amdgcn_raw_buffer_load_b128(rs, float_off * 4, 0, COH ? kCoherentBits : 0));
+}
+template <bool COH>
+__device__ __forceinline__ float load1_partial(__amdgpu_buffer_rsrc_t rs, int32_t float_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, float_off * 4, 0, COH ? kCoherentBits : 0));
 }
 __device__ __forceinline__ void store4_coherent(__amdgpu_buffer_rsrc_t rs, int32_t float_off, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, float_off * 4, 0, kCoherentBits);
@@ -77,9 +90,10 @@ __device__ __forceinline__ void merge_one(const float *__restrict__ sp_m, const 
 // rescale), so the merge costs one memory round trip for P <= 8. The
 // partials were written by other workgroups of the same launch (device-
 // coherent stores), so every load is device-coherent too.
+template <bool COH>
 __device__ __forceinline__ void merge_row(const float *__restrict__ sp_m, const float *__restrict__ sp_l,
                                           const float *__restrict__ sp_o, int64_t row, int32_t H, int32_t P,
-                                          uint16_t *__restrict__ out, float *__restrict__ lse) {
+                                          int32_t mls, uint16_t *__restrict__ out, float *__restrict__ lse) {
   const float NEG_INF = -__builtin_inff();
   const int t = threadIdx.x, h = t >> 4, e0 = 8 * (t & 15);
   if (h >= H) return;
@@ -89,16 +103,17 @@ __device__ __forceinline__ void merge_row(const float *__restrict__ sp_m, const 
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   const __amdgpu_buffer_rsrc_t ro = row_rsrc(sp_o + row * H * P * kDim, H * P * kDim);
   // (m, l) of 4 partitions per 16-byte load when P is a multiple of 4 (the
-  // row's (m, l) arrays are then 16-byte aligned); reads past the row's last
-  // head return 0 (descriptor bound) and, like every u >= P - p0, weigh nothing
-  const bool ml4 = (P & 3) == 0;
-  const __amdgpu_buffer_rsrc_t rm = row_rsrc(sp_m + row * H * P, H * P), rl = row_rsrc(sp_l + row * H * P, H * P);
+  // row's (m, l) arrays, mls floats apart, are then 16-byte aligned); reads past
+  // the row's last head return 0 (descriptor bound) and, like every u >= P - p0,
+  // weigh nothing
+  const bool ml4 = (P & 3) == 0 && (mls & 3) == 0;
+  const __amdgpu_buffer_rsrc_t rm = row_rsrc(sp_m + row * mls, H * P), rl = row_rsrc(sp_l + row * mls, H * P);
   for (int p0 = 0; p0 < P; p0 += 8) {
     float m[8], l[8];
     f32x4 o[8][2];
     if (ml4) {
-      const f32x4 m0 = load4_coherent(rm, h * P + p0), m1 = load4_coherent(rm, h * P + p0 + 4);
-      const f32x4 l0 = load4_coherent(rl, h * P + p0), l1 = load4_coherent(rl, h * P + p0 + 4);
+      const f32x4 m0 = load4_partial<COH>(rm, h * P + p0), m1 = load4_partial<COH>(rm, h * P + p0 + 4);
+      const f32x4 l0 = load4_partial<COH>(rl, h * P + p0), l1 = load4_partial<COH>(rl, h * P + p0 + 4);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         m[u] = m0[u];
@@ -110,8 +125,8 @@ __device__ __forceinline__ void merge_row(const float *__restrict__ sp_m, const 
 #pragma unroll
       for (int u = 0; u < 8; ++u) {               // clamped, unconditional
         const int pp = min(p0 + u, P - 1);
-        m[u] = load1_coherent(rm, h * P + pp);
-        l[u] = load1_coherent(rl, h * P + pp);
+        m[u] = load1_partial<COH>(rm, h * P + pp);
+        l[u] = load1_partial<COH>(rl, h * P + pp);
       }
     }
 #pragma unroll
@@ -119,7 +134,7 @@ __device__ __forceinline__ void merge_row(const float *__restrict__ sp_m, const 
       const int pp = min(p0 + u, P - 1);
       const int32_t off = (h * P + pp) * kDim + e0;
 #pragma unroll
-      for (int k = 0; k < 2; ++k) o[u][k] = load4_coherent(ro, off + 4 * k);
+      for (int k = 0; k < 2; ++k) o[u][k] = load4_partial<COH>(ro, off + 4 * k);
     }
     float Mc = M;
 #pragma unroll

@@ -182,10 +182,10 @@ template <bool COH>
 __device__ __forceinline__ void reuse_store_wg(const CacheView &c, const float *__restrict__ k_new,
                                                const float *__restrict__ v_new, const void *__restrict__ q,
                                                int q_dtype, int H, uint8_t *__restrict__ q8,
-                                               uint32_t *__restrict__ counters, int q_rows, int row) {
+                                               uint64_t *__restrict__ counters, int q_rows, int row) {
   const int b = row / q_rows, j = row % q_rows;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (counters && tid == 0) st_u32<COH>(counters + row, 0u);
+  if (counters && tid == 0) st_u64<COH>(counters + row, 0ull);
   if (wave < 2) {
     const float *src = wave == 0 ? k_new : v_new;
     if (!src) return;

@@ -520,7 +520,7 @@ __device__ __forceinline__ void index_score_wg(const CacheView &c, const uint16_
   // the attention launch's merge counters for sequence b (at the end: in the
   // prologue this would split the kernel-argument loads into two round trips)
   if (st.counters && gy == ny - 1)
-    for (int i = threadIdx.x; i < q; i += 64 * NW) st.counters[b * q + i] = 0u;
+    for (int i = threadIdx.x; i < q; i += 64 * NW) st_u64<COH>(st.counters + b * q + i, 0ull);
 }
 
 template <int MT, int FMT, int NW, int PPW, int S>

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void k_pack_q(const void *__restrict__ q, int 
 __global__ __launch_bounds__(256) void k_reuse_store(CacheView c, const float *__restrict__ k_new,
                                                      const float *__restrict__ v_new, const void *__restrict__ q,
                                                      int q_dtype, int H, uint8_t *__restrict__ q8,
-                                                     uint32_t *__restrict__ counters, int q_rows) {
+                                                     uint64_t *__restrict__ counters, int q_rows) {
   reuse_store_wg<false>(c, k_new, v_new, q, q_dtype, H, q8, counters, q_rows, blockIdx.x);
 }
 
@@ -60,7 +60,7 @@ hipError_t launch_zero(uint32_t *p, size_t n, hipStream_t s) {
 }
 
 hipError_t launch_reuse_store(const CacheView &c, const float *k_new, const float *v_new, const void *q, int q_dtype,
-                              int32_t H, uint8_t *q8, uint32_t *counters, int32_t B, int32_t q_rows, hipStream_t s) {
+                              int32_t H, uint8_t *q8, uint64_t *counters, int32_t B, int32_t q_rows, hipStream_t s) {
   if (B * q_rows == 0) return hipSuccess;
   hipLaunchKernelGGL(k_reuse_store, dim3((unsigned)(B * q_rows)), dim3(256), 0, s, c, k_new, v_new, q, q_dtype, H, q8,
                      counters, q_rows);
