@@ -34,6 +34,8 @@ typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 
 __device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
@@ -132,6 +134,20 @@ __device__ __forceinline__ void fp4x8_to_bf16_nv(uint32_t packed, float sc, uint
   MXS_NV_PAIR(3);
 }
 #undef MXS_NV_PAIR
+
+// The same as four f16 pairs, for the f16 MFMA: the codes widen exactly to
+// f16 (v_cvt_scalef32_pk_f16_fp4 with scale 1) and one packed f16 multiply
+// applies the block scale (sc: the e4m3 value in both halves); the product is
+// exact in f16 too (<= 6 significant bits, 2^-10 .. 2688, all normal).
+#define MXS_NV16_PAIR(k)                                                                                   \
+  out[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, k) * sc)
+__device__ __forceinline__ void fp4x8_to_f16_nv(uint32_t packed, f16x2 sc, uint32_t out[4]) {
+  MXS_NV16_PAIR(0);
+  MXS_NV16_PAIR(1);
+  MXS_NV16_PAIR(2);
+  MXS_NV16_PAIR(3);
+}
+#undef MXS_NV16_PAIR
 
 // Four e4m3 codes (one dword) -> two dwords of bf16 pairs, element order kept
 // (v_cvt_scalef32_pk_bf16_fp8 with scale 1: exact, e4m3 has 3 mantissa bits;

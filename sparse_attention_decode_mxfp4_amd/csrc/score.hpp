@@ -7,7 +7,8 @@
 //   S[b][j][i] = max over t in block i, t <= pos_j, of
 //                sum_h w[b][j][h] * max(0, q_idx[b][j][h] . k_idx[t])
 //
-// The contraction q_idx . k runs on the bf16 MFMA (v_mfma_f32_16x16x32_bf16):
+// The contraction q_idx . k runs on the bf16 MFMA (v_mfma_f32_16x16x32_bf16;
+// NVFP4 keys on the f16 one, see query_rows_f16):
 // M = query rows x index heads (4 A-rows per query row, heads padded to 4),
 // N = 16 tokens, K = head_dim. The page's e2m1 keys are widened to bf16 in
 // registers with their e8m0 group scale (v_cvt_scalef32_pk_bf16_fp4; bf16
@@ -127,9 +128,10 @@ __device__ __forceinline__ void dma_chunk(uint8_t *stage, const uint8_t *page, i
   }
 }
 
-// B operand (k-step s) of tile nt: the lane's key elements 32 kg + 8 s .. + 7 as bf16.
+// B operand (k-step s) of tile nt: the lane's key elements 32 kg + 8 s .. + 7
+// as bf16 (MXFP4, FP8) or f16 (NVFP4) bits.
 template <int FMT>
-__device__ __forceinline__ void key_operands(const uint8_t *stage, int nt, int n, int kg, int lane, bf16x8 Bk[4],
+__device__ __forceinline__ void key_operands(const uint8_t *stage, int nt, int n, int kg, int lane, u32x4 Bk[4],
                                              float &ksc) {
   if constexpr (FMT == 0) {
     const u32x4 kd = *reinterpret_cast<const u32x4 *>(stage + 1024 * nt + 16 * lane);
@@ -138,18 +140,20 @@ __device__ __forceinline__ void key_operands(const uint8_t *stage, int nt, int n
     for (int s = 0; s < 4; ++s) {
       uint32_t w4[4];
       fp4x8_to_bf16(kd[s], sf, w4);
-      Bk[s] = __builtin_bit_cast(bf16x8, u32x4{w4[0], w4[1], w4[2], w4[3]});
+      Bk[s] = u32x4{w4[0], w4[1], w4[2], w4[3]};
     }
     ksc = 1.0f;
   } else if constexpr (FMT == 2) {
     const u32x4 kd = *reinterpret_cast<const u32x4 *>(stage + 1024 * nt + 16 * lane);
-    // the e4m3 scales of blocks 2 kg and 2 kg + 1 of token 16 nt + n
-    const float2 bs = e4m3x2_f32(*reinterpret_cast<const uint16_t *>(stage + Chunk<2>::kCodes + 8 * (16 * nt + n) + 2 * kg));
+    // the e4m3 scales of blocks 2 kg and 2 kg + 1 of token 16 nt + n, as f16 (exact)
+    const f16x2 bs = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+        *reinterpret_cast<const uint16_t *>(stage + Chunk<2>::kCodes + 8 * (16 * nt + n) + 2 * kg), 1.0f, false);
+    const f16x2 s0 = {bs.x, bs.x}, s1 = {bs.y, bs.y};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       uint32_t w4[4];
-      fp4x8_to_bf16_nv(kd[s], s < 2 ? bs.x : bs.y, w4);
-      Bk[s] = __builtin_bit_cast(bf16x8, u32x4{w4[0], w4[1], w4[2], w4[3]});
+      fp4x8_to_f16_nv(kd[s], s < 2 ? s0 : s1, w4);
+      Bk[s] = u32x4{w4[0], w4[1], w4[2], w4[3]};
     }
     ksc = *reinterpret_cast<const float *>(stage + Chunk<2>::kTok + 4 * (16 * nt + n));
   } else {
@@ -159,11 +163,54 @@ __device__ __forceinline__ void key_operands(const uint8_t *stage, int nt, int n
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const uint2 x = e4m3x4_to_bf16(kd[2 * hh]), y = e4m3x4_to_bf16(kd[2 * hh + 1]);
-        Bk[2 * cc + hh] = __builtin_bit_cast(bf16x8, u32x4{x.x, x.y, y.x, y.y});
+        Bk[2 * cc + hh] = u32x4{x.x, x.y, y.x, y.y};
       }
     }
     ksc = *reinterpret_cast<const float *>(stage + Chunk<1>::kCodes + 4 * (16 * nt + n));
   }
+}
+
+// NVFP4 keys take the f16 MFMA: their widening is then one convert and one
+// packed multiply per pair (bf16 has no packed multiply here, and the scaled
+// converts apply only a power of two). The query rows become f16 once per
+// workgroup: each A row (query row, index head) times 2^e, e chosen so that
+// its largest magnitude lies in [2^14, 2^15) (e clamped to [-113, 126] at the
+// ends of the bf16 range). bf16 carries 8 significant bits and f16 11, so
+// every element of at least 2^-28 times its row's largest lands in f16's
+// normal range and converts exactly; a smaller one becomes an f16 subnormal
+// (steps of 2^-24 in the scaled units), off by less than 2^-38 of the row's
+// largest. The weights of the result rows
+// take 2^-e back (a power of two: exact), so the scores are those of the
+// bf16 query to that precision. A holds bf16 bits on entry, f16 bits after.
+template <int MT>
+__device__ __forceinline__ void query_rows_f16(u32x4 (&A)[MT][4], float (&wv)[MT][4], int n, int kg) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    uint32_t a = 0u;                                 // the row's largest |q| (fp32 bits order like values)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) a = max(a, max((A[mt][s][k] << 16) & 0x7FFFFFFFu, A[mt][s][k] & 0x7FFF0000u));
+    a = max(a, xor_lane<16>(a));                     // the 4 lane groups hold the row's 128 elements
+    a = max(a, xor_lane<32>(a));
+    const int e = a == 0u ? 0 : min(max(141 - (int)(a >> 23), -113), 126);
+    const float f = u2f((uint32_t)(127 + e) << 23);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t d = A[mt][s][k];
+        const f16x2 h = {(_Float16)(u2f(d << 16) * f), (_Float16)(u2f(d & 0xFFFF0000u) * f)};
+        A[mt][s][k] = __builtin_bit_cast(uint32_t, h);
+      }
+    // result rows 16 mt + 4 kg + i are A rows 16 mt + n' with n' = 4 kg + i: lane n' holds their e
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ei = __shfl(e, 4 * kg + i);
+      wv[mt][i] *= u2f((uint32_t)(127 - ei) << 23);
+    }
+  }
+  (void)n;
 }
 
 // The decode step's new K / V / index rows and e4m3 query, spread over the
@@ -340,7 +387,7 @@ __device__ __forceinline__ void index_score_wg(const CacheView &c, const uint16_
 
   // A operand: q_idx rows m = 16 mt + n -> (query row m / 4, head m % 4); rows
   // past q or H_I are zero (their load reads row 0 and is discarded)
-  bf16x8 A[MT][4];
+  u32x4 A[MT][4];                                    // bf16 bits (f16 for NVFP4 keys, below)
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = 16 * mt + n, jA = m >> 2, hA = m & 3;
@@ -350,7 +397,7 @@ __device__ __forceinline__ void index_score_wg(const CacheView &c, const uint16_
     for (int s = 0; s < 4; ++s) {
       u32x4 v = *reinterpret_cast<const u32x4 *>(src + 8 * s);
       if (!ok) v = u32x4{0u, 0u, 0u, 0u};
-      A[mt][s] = __builtin_bit_cast(bf16x8, v);
+      A[mt][s] = v;
     }
   }
   // result rows 16 mt + 4 kg + i -> query row 4 mt + kg, index head i
@@ -393,11 +440,12 @@ __device__ __forceinline__ void index_score_wg(const CacheView &c, const uint16_
 #pragma unroll
     for (int h = 0; h < 4; ++h) asm volatile("" ::"v"(wv[mt][h]));
 #pragma unroll
-    for (int s = 0; s < 4; ++s) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, A[mt][s])));
+    for (int s = 0; s < 4; ++s) asm volatile("" ::"v"(A[mt][s]));
   }
   asm volatile("" ::"v"(praw));
   asm volatile("" ::"v"(sw.row.x), "v"(sw.row.y), "v"(sw.qe));
   asm volatile("" ::"s"(L) : "memory");
+  if constexpr (FMT == 2) query_rows_f16<MT>(A, wv, n, kg);
 
   const int lim = min((L + kTokens - 1) / kTokens, (int)c.stride);    // pages holding tokens
   auto quant_share = [&]() {
@@ -439,7 +487,7 @@ __device__ __forceinline__ void index_score_wg(const CacheView &c, const uint16_
                          float (&rmax)[MT]) {
 #pragma unroll 2
       for (int nt = 0; nt < 4; ++nt) {
-        bf16x8 Bk[4];
+        u32x4 Bk[4];
         float ksc;
         key_operands<FMT>(stage, nt, n, kg, lane, Bk, ksc);
         const int t = p * kTokens + 64 * h + 16 * nt + n;
@@ -447,7 +495,14 @@ __device__ __forceinline__ void index_score_wg(const CacheView &c, const uint16_
         for (int mt = 0; mt < MT; ++mt) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][s], Bk[s], acc, 0, 0, 0);
+          for (int s = 0; s < 4; ++s) {
+            if constexpr (FMT == 2)
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, A[mt][s]),
+                                                           __builtin_bit_cast(f16x8, Bk[s]), acc, 0, 0, 0);
+            else
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[mt][s]),
+                                                            __builtin_bit_cast(bf16x8, Bk[s]), acc, 0, 0, 0);
+          }
           float v = 0.f;
 #pragma unroll
           for (int hd = 0; hd < 4; ++hd) v += wv[mt][hd] * relu1(FMT != 0 ? acc[hd] * ksc : acc[hd]);
