@@ -180,6 +180,31 @@ def test_index_scores(mx, name):
         PT.check_scores(S[b], Sr, Sa, OI.n_candidates(L, wl.q))
 
 
+def test_index_scores_nvfp4_query_magnitudes(mx):
+    """NVFP4 index keys run on the f16 MFMA with each query row scaled by a
+    power of two into f16's range: rows scaled by 2^-60 .. 2^60, and a row
+    whose elements span 2^-40 .. 1 of its largest, score within the usual
+    bound of the oracle's bf16 arithmetic."""
+    inp, pools, cache, t = _setup(mx, "nvfp4")
+    wl = inp.wl
+    rng = np.random.default_rng(21)
+    q = OF.bf16_to_f64(inp.q_idx)                                  # [B][q][H_I][128]
+    q *= np.ldexp(1.0, rng.integers(-60, 61, size=q.shape[:3]))[..., None]
+    q[0, 0, 0] *= np.ldexp(1.0, -rng.integers(0, 41, size=128))    # one row spanning 2^-40 .. 1
+    inp.q_idx = W.bf16_bits(q.astype(np.float32))
+    assert np.array_equal(OF.bf16_to_f64(inp.q_idx), q)            # the scaling is exact in bf16
+    import workloads.gpu as WG
+    t = WG.step_tensors(inp)
+    S = mx.index_score(cache, t["q_idx"], t["w"]).cpu().numpy().astype(np.float64)
+    ref_pool = OS.build_cache(inp, "idx", wl.idx_format)
+    for b in range(wl.B):
+        L = int(inp.contexts[b])
+        kI = OF.READ[wl.idx_format](ref_pool, inp.page_table[b], L)
+        Sr = OI.index_scores(kI, q[b], inp.w[b].astype(np.float64), L)
+        Sa = PT.score_bound(kI, q[b], inp.w[b].astype(np.float64), L)
+        PT.check_scores(S[b], Sr, Sa, OI.n_candidates(L, wl.q))
+
+
 def test_index_score_one_hot_structure(mx):
     """A single non-zero key element and a one-hot query pin the element,
     token and head mapping of the scorer."""
