@@ -101,6 +101,22 @@ def test_decode_step_partition_counts(mx, P):
     check_step(inp, g, [0, 1])
 
 
+@pytest.mark.parametrize("kw,P", [
+    (dict(B=1, q=6, topk=16), 4),     # 24 workgroups dealt to the XCDs in runs of 3: each row's 4 partitions split
+    (dict(B=1, q=3, topk=16), 3),     # 9 workgroups (not a multiple of 8): every row spread over several XCDs
+    (dict(B=2, q=8, topk=32), 8),     # runs of 16: every row on one XCD (its merge reads through that L2)
+])
+def test_decode_step_rows_on_one_or_several_xcds(mx, kw, P):
+    """The row merge reads its partials through the L2 only when every
+    partition of the row ran on the merging workgroup's XCD, and with
+    device-coherent loads otherwise: both paths, and rows that straddle two
+    XCDs' runs of work items."""
+    wl = W.WORKLOADS["mxfp4_65k"].with_(name="xcd", **kw)
+    inp = W.make_inputs(wl)
+    g = run_step(mx, inp, num_partitions=P)
+    check_step(inp, g, range(wl.B))
+
+
 @pytest.mark.parametrize("kw", [
     dict(ctx_rule=("list", (9, 130, 1000, 4096)), B=4, q=8, H=16, topk=16),      # contexts near q, ragged
     dict(ctx_rule=("list", (8, 300)), B=2, q=8, H=1, H_I=1, topk=64),            # L == q; H = 1; H_I = 1
