@@ -22,9 +22,7 @@ static void launch_mt(const CacheView &c, const uint16_t *q_idx, const float *w,
       launch_shape<FMT, MT, Shape<4, 2, 2>>(c, q_idx, w, B, q, H_I, scores, st, s);
     else
       launch_shape<FMT, MT, Shape<4, 1, 2>>(c, q_idx, w, B, q, H_I, scores, st, s);
-  } else if (pages >= 256 * 32) {         // >= 256 workgroups of 32 pages (MXFP4; NVFP4 takes the same shapes)
-    launch_shape<FMT, MT, Shape<4, 8, 3>>(c, q_idx, w, B, q, H_I, scores, st, s);
-  } else if (pages >= 256 * 16) {
+  } else if (pages >= 256 * 16) {         // >= 256 workgroups of 16 pages, two per CU (MXFP4; NVFP4 alike)
     launch_shape<FMT, MT, Shape<4, 4, 2>>(c, q_idx, w, B, q, H_I, scores, st, s);
   } else {
     launch_shape<FMT, MT, Shape<4, 1, 2>>(c, q_idx, w, B, q, H_I, scores, st, s);

@@ -56,11 +56,15 @@ template <> struct Chunk<1> { static constexpr int kCodes = 8192, kBytes = 8192 
 template <> struct Chunk<2> { static constexpr int kCodes = 4096, kTok = 4096 + 512, kBytes = 4096 + 512 + 256, kDma = 7, kPage = kNvPageBytes; };
 
 // Launch shapes: waves per workgroup, pages per wave, LDS stages per wave.
-// Measured on MI355X (MXFP4 index, 4 sequences): 4 x 8 x 3 is fastest once
-// the grid still gives every CU a workgroup (256 workgroups at 2048 pages per
-// sequence: 16.9 us against 17.6 us for 4 x 4 x 2 and 18.3 us for 4 x 2 x 2);
-// smaller page tables want more, shorter workgroups (512 pages: 4 x 1 x 2 at
-// 6.9 us against 7.1 us for 4 x 2 x 2 and 9.6 us for 4 x 4 x 2).
+// Measured on MI355X, each shape timed in one session at loaded clocks
+// (stand-alone scorer / full step): at >= 4096 pages, 4 x 4 x 2 (two
+// workgroups per CU) against 4 x 8 x 3 (one per CU): 4 sequences x 2048
+// pages 17.6 / 34.2-34.5 us against 17.9 / 34.7, the same over NVFP4 pages
+// 21.6 / 39.3-40.1 against 22.1 / 42.7, 32 ragged sequences (8K-256K)
+// 80.1 / 115.4 against 85.0 / 122.6; 4 x 2 x 2, 4 x 4 x 3, 4 x 8 x 2 and
+// 8 x 4 x 2 were no better anywhere. Smaller page tables want short
+// workgroups (512 pages: 4 x 1 x 2 at 6.9 us against 7.1 us for 4 x 2 x 2
+// and 9.6 us for 4 x 4 x 2).
 template <int NW_, int PPW_, int S_> struct Shape {
   static constexpr int kWaves = NW_, kPages = PPW_, kStages = S_;
 };

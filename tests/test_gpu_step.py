@@ -199,7 +199,8 @@ def test_decode_step_long_with_empty_partitions(mx, b):
     dict(B=2, ctx_rule=("list", (516, 1028)), topk=16),
     # 4 x 4 pages (16-page workgroups; 4096 pages in all): boundaries at 2048-token multiples
     dict(B=4, ctx_rule=("list", (131072, 2052, 4100, 8196)), topk=16),
-    # 4 x 8 pages (32-page workgroups; 8192 pages in all): boundaries at 4096-token multiples
+    # the same shape at the headline's 8192 pages (the single-launch step's 32-page
+    # scoring workgroups have boundaries at 4096-token multiples: the same positions)
     dict(B=4, ctx_rule=("list", (262144, 4100, 8196, 65540)), topk=32),
 ])
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
@@ -216,7 +217,7 @@ def test_decode_step_new_rows_straddle_scorer_workgroups(mx, kw, fmt):
 
 def test_decode_step_wide_page_table(mx):
     """The 65K workload with its page table padded to 4096 entries per
-    sequence (-1 past each sequence): the scorer's 32-page workgroups past the
+    sequence (-1 past each sequence): the scorer's 16-page workgroups past the
     context and the selection's 32-candidates-per-thread variant."""
     inp, g = cached_run(mx, "mxfp4_65k", table_stride=4096)
     assert inp.max_pages == 4096
