@@ -11,7 +11,9 @@ cache) and are captured in one HIP graph of K steps, replayed once. The default 
 the 256K-context one: B = 4 sequences x q = 8 query rows (1 + 7 drafts), 16
 query heads per KV head, head_dim 128, MXFP4 K / V / index caches, top-k 32.
 
-Inputs are resident in HBM before timing starts, and the GPU has been kept
+The replicas share one page table and one context-length vector (the layers
+of a decode share the sequences' block table); each has its own K / V / index
+pools. Inputs are resident in HBM before timing starts, and the GPU has been kept
 busy with untimed step replays for --settle-ms of wall time (it lowers its
 clocks when idle; each later kernel timing is preceded by its own shorter
 settle), then the W warmup steps run. Each timed step runs on the
@@ -239,7 +241,10 @@ def main():
     t = WG.step_tensors(inp)
     R = max(1, args.replicas)
     replicas = [pools0] + [{s: p.clone() for s, p in pools0.items()} for _ in range(R - 1)]
-    caches = [WG.make_cache(inp, p) for p in replicas]
+    # the replicas share one page table and context-length vector, as the layers
+    # of a decode step share the sequences' block table; each has its own pools
+    c0 = WG.make_cache(inp, replicas[0])
+    caches = [c0] + [WG.make_cache(inp, p, table=c0.page_table, ctx=c0.context_lens) for p in replicas[1:]]
     tables = [torch.empty((wl.B, wl.q, wl.topk), dtype=torch.int32, device="cuda") for _ in range(R)]
     steps = [mx.DecodeStep(c, t["query"], t["q_idx"], t["w"], wl.topk, wl.sm_scale, k_new=t.get("k_new"),
                            v_new=t.get("v_new"), idx_new=t.get("idx_new"), block_table_out=tb)

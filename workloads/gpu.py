@@ -44,10 +44,15 @@ def fill_prefix(inp: StepInputs, pools, seqs=None, chunk_rows=1 << 20, device="c
     return pools
 
 
-def make_cache(inp: StepInputs, pools, device="cuda") -> mx.Cache:
+def make_cache(inp: StepInputs, pools, device="cuda", table=None, ctx=None) -> mx.Cache:
+    """A cache view over `pools`; `table` / `ctx` (device tensors) let several
+    caches share one page table and one context-length vector, as the layers of
+    a decode step share the sequences' block table."""
     wl = inp.wl
-    table = torch.from_numpy(inp.page_table).to(device)
-    ctx = torch.from_numpy(inp.contexts.astype(np.int32)).to(device)
+    if table is None:
+        table = torch.from_numpy(inp.page_table).to(device)
+    if ctx is None:
+        ctx = torch.from_numpy(inp.contexts.astype(np.int32)).to(device)
     return mx.Cache(pools["k"], pools["v"], pools["idx"], table, ctx, wl.kv_format, wl.idx_format)
 
 
