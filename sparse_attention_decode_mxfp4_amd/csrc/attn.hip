@@ -40,8 +40,10 @@
 //   MFMA with the codes widened exactly to bf16 and the token scale applied to
 //   the dot product; PV folds the token scale into P.
 // * NVFP4 KV (e2m1 in 16-element blocks with e4m3 block scales, per-token fp32
-//   scale, bf16 query): the MXFP4 lane layout, the codes widened to bf16 times
-//   their block scale (exact), the token scale handled as for FP8.
+//   scale, bf16 query): the MXFP4 lane layout, the codes widened times their
+//   block scale (exact): K to f16 for QK on the f16 MFMA against the query
+//   scaled per head into f16 (query_operands_f16), V to bf16 for PV; the token
+//   scale handled as for FP8.
 #include "common.hpp"
 #include "launch.hpp"
 #include "topk.hpp"
@@ -244,6 +246,40 @@ __device__ __forceinline__ void query_operands(const QueryRegs<FMT> &q, int H, i
   }
 }
 
+// NVFP4: B operand of QK as f16, for the f16 MFMA (the keys widen to f16 in
+// two instructions per pair, see fp4x8_to_f16_nv). Head n's 128 bf16 query
+// elements (this lane: 32 of them, the other 32-element groups in lanes
+// n + 16 kg) are scaled by 2^e so that the head's largest magnitude lies in
+// [2^14, 2^15) (e clamped to [-113, 126] at the ends of the bf16 range):
+// bf16's 8 significant bits fit f16's 11, so every element of at least 2^-28
+// times the head's largest converts exactly and smaller ones to within 2^-38
+// of it. The logits take inv_scale = 2^-e back (exact). Heads >= H are zero.
+__device__ __forceinline__ void query_operands_f16(const QueryRegs<2> &q, int H, int n, f16x8 qh[4],
+                                                   float &inv_scale) {
+  uint32_t a = 0u;                                 // the head's largest |q| (fp32 bits order like values)
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a = max(a, max((q.c[s][k] << 16) & 0x7FFFFFFFu, q.c[s][k] & 0x7FFF0000u));
+  a = max(a, xor_lane<16>(a));
+  a = max(a, xor_lane<32>(a));
+  const int e = a == 0u ? 0 : min(max(141 - (int)(a >> 23), -113), 126);
+  const float f = u2f((uint32_t)(127 + e) << 23);
+  inv_scale = u2f((uint32_t)(127 - e) << 23);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    u32x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t d = q.c[s][k];
+      const f16x2 h = {(_Float16)(u2f(d << 16) * f), (_Float16)(u2f(d & 0xFFFF0000u) * f)};
+      v[k] = __builtin_bit_cast(uint32_t, h);
+    }
+    if (n >= H) v = u32x4{0u, 0u, 0u, 0u};
+    qh[s] = __builtin_bit_cast(f16x8, v);
+  }
+}
+
 // The wave's token range of one selected block (page `phys`, 16 NT tokens
 // from page token toff, at positions t0 ..) folded into this wave's online
 // softmax state for head n = lane % 16: m_run (log2 units: the logits times
@@ -265,7 +301,12 @@ __device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t
 #pragma unroll
   for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(qc.c[s]));
   bf16x8 qbf[4];
-  query_operands<FMT>(qc, H, n, qbf);
+  f16x8 qh[4];                                    // NVFP4: the f16 query (head n scaled by 2^e)
+  float q_inv = 1.0f;                             // NVFP4: 2^-e
+  if constexpr (FMT == 2)
+    query_operands_f16(qc, H, n, qh, q_inv);
+  else
+    query_operands<FMT>(qc, H, n, qbf);
 
   // ---- QK: scores (log2 units) of tokens 16 nt + 4 kg + i for head n
   float sc[NT][4];
@@ -273,8 +314,12 @@ __device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t
   for (int nt = 0; nt < NT; ++nt) {
     const bool live = FULL || t0 + 16 * nt + n <= pos;       // the lane's A row (token 16 nt + n)
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float2 kbs = make_float2(1.f, 1.f);             // NVFP4: blocks 2 kg, 2 kg + 1 (1.0 = 0x38 where masked)
-    if constexpr (FMT == 2) kbs = e4m3x2_f32(live ? r.kb[nt] : 0x3838u);
+    f16x2 kb0, kb1;                                 // NVFP4: blocks 2 kg, 2 kg + 1 as f16 (1.0 = 0x38 where masked)
+    if constexpr (FMT == 2) {
+      const f16x2 bs = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(live ? r.kb[nt] : 0x3838u, 1.0f, false);
+      kb0 = f16x2{bs.x, bs.x};
+      kb1 = f16x2{bs.y, bs.y};
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u32x4 a;
@@ -284,7 +329,7 @@ __device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t
         a = u32x4{w4[0], w4[1], w4[2], w4[3]};
       } else if constexpr (FMT == 2) {
         uint32_t w4[4];
-        fp4x8_to_bf16_nv(live ? r.k[nt][s] : 0u, s < 2 ? kbs.x : kbs.y, w4);
+        fp4x8_to_f16_nv(live ? r.k[nt][s] : 0u, s < 2 ? kb0 : kb1, w4);
         a = u32x4{w4[0], w4[1], w4[2], w4[3]};
       } else {
         const u32x4 &src = r.k[nt][s >> 1];
@@ -292,11 +337,14 @@ __device__ __forceinline__ void attend_block(const CacheView &c, int phys, int t
         const uint2 y = e4m3x4_to_bf16(live ? src[2 * (s & 1) + 1] : 0u);
         a = u32x4{x.x, x.y, y.x, y.y};
       }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qbf[s], acc, 0, 0, 0);
+      if constexpr (FMT == 2)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), qh[s], acc, 0, 0, 0);
+      else
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qbf[s], acc, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float x = acc[i] * qk_scale2;
+      float x = (FMT == 2 ? acc[i] * q_inv : acc[i]) * qk_scale2;
       if constexpr (FMT != 0) x *= r.ks[nt][i];
       sc[nt][i] = (FULL || t0 + 16 * nt + 4 * kg + i <= pos) ? x : NEG_INF;
     }
