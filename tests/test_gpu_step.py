@@ -215,12 +215,14 @@ def test_decode_step_new_rows_straddle_scorer_workgroups(mx, kw, fmt):
     check_step(inp, g, range(wl.B))
 
 
-def test_decode_step_wide_page_table(mx):
+@pytest.mark.parametrize("stride", [4096, 8192])
+def test_decode_step_wide_page_table(mx, stride):
     """The 65K workload with its page table padded to 4096 entries per
-    sequence (-1 past each sequence): the scorer's 16-page workgroups past the
-    context and the selection's 32-candidates-per-thread variant."""
-    inp, g = cached_run(mx, "mxfp4_65k", table_stride=4096)
-    assert inp.max_pages == 4096
+    sequence, and to the largest table the library takes (8192 pages, 1M
+    tokens), with -1 past each sequence: the scorer's 16-page workgroups past
+    the context and the selection's 32-candidates-per-thread variant."""
+    inp, g = cached_run(mx, "mxfp4_65k", table_stride=stride)
+    assert inp.max_pages == stride
     check_step(inp, g, range(inp.wl.B))
 
 
