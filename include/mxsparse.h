@@ -194,15 +194,21 @@ size_t mxs_score_workspace_bytes(int32_t B, int32_t q, int32_t page_table_stride
  *         FP8 or NVFP4 KV: bf16 bits (q_dtype MXS_BF16) [B][q][H][128]; 16 B aligned
  *   block_table [B][q][topk] int32 block ids (-1 = empty slot)
  *   sp_m, sp_l  [B][q][H][P] fp32;  sp_o [B][q][H][P][128] fp32 (outputs)
- * P = num_partitions in 1..64 (0: mxs_default_partitions). */
+ * P = num_partitions in 1..64 (0: mxs_default_partitions_for(B, q_rows, topk,
+ * cache->kv_format)). */
 int sparse_split_attn(const mxs_cache *cache, const void *q, int32_t q_dtype,
                       const int32_t *block_table, int32_t B, int32_t q_rows, int32_t H,
                       int32_t topk, int32_t num_partitions, float sm_scale, float *sp_m,
                       float *sp_l, float *sp_o, void *stream);
-/* The partition count the library takes for num_partitions = 0:
- * min(ceil(topk / 4), max(1, 256 / (B q_rows))), clamped to 1..64 — one block
- * per wave of a 4-wave workgroup, but no more workgroups than MI355X has CUs
- * once the rows alone fill it (a choice of this library; the pages fix none). */
+/* The partition count the library takes for num_partitions = 0 over K / V
+ * pages of format kv_format: min(ceil(topk / 4), max(1, 256 / (B q_rows))),
+ * clamped to 1..64 — one block per wave of a 4-wave workgroup, but no more
+ * workgroups than MI355X has CUs once the rows alone fill it — with
+ * ceil(topk / 2) in place of ceil(topk / 4) for FP8 K / V, whose pages are
+ * twice as large (two blocks per workgroup). A choice of this library; the
+ * pages fix none. Unknown formats take the MXFP4 rule.
+ * mxs_default_partitions: the same for MXFP4 (and NVFP4) K / V. */
+int mxs_default_partitions_for(int32_t B, int32_t q_rows, int32_t topk, int32_t kv_format);
 int mxs_default_partitions(int32_t B, int32_t q_rows, int32_t topk);
 
 /* ---- 6. merge ------------------------------------------------------------
@@ -241,7 +247,9 @@ typedef struct {
  * mxs_workspace_bytes(...) bytes, 256 B aligned; its contents need no
  * initialization and are scratch after the call (it holds the per-row merge
  * counters, cleared by the first launch), so two calls in flight at once must
- * not share one. */
+ * not share one. mxs_workspace_bytes with num_partitions = 0 sizes for the
+ * larger default over the formats (mxs_default_partitions_for), enough for
+ * any cache format. */
 int decode_step(const mxs_step *step, void *ws, size_t ws_bytes, void *stream);
 size_t mxs_workspace_bytes(int32_t B, int32_t q, int32_t H, int32_t H_I, int32_t topk,
                            int32_t page_table_stride, int32_t num_partitions);

@@ -24,6 +24,7 @@ PAGE_BYTES = {"mxfp4": 8704, "fp8": 16896, "nvfp4": 9728}
 EXPORTS = [
     "mxfp4_row_store", "fp8_row_store", "nvfp4_row_store", "pack_q_e4m3", "index_score", "topk_blocks",
     "index_score_topk", "mxs_score_workspace_bytes", "sparse_split_attn", "mxs_default_partitions",
+    "mxs_default_partitions_for",
     "lse_merge", "decode_step", "decode_step_reuse", "mxs_workspace_bytes", "mxs_status_str", "mxs_last_error",
     "mxs_abi_version", "mxs_read_index_pages", "decode_step_noalloc", "mxs_workspace_init",
     "decode_step_one_launch", "decode_step_reuse_one_launch",
@@ -89,6 +90,7 @@ def lib() -> ctypes.CDLL:
             "decode_step_one_launch": [P, P, SZ, P],
             "mxs_read_index_pages": [P, I32, P, P],
             "mxs_default_partitions": [I32, I32, I32],
+            "mxs_default_partitions_for": [I32, I32, I32, I32],
             "mxs_score_workspace_bytes": [I32, I32, I32],
             "mxs_workspace_bytes": [I32, I32, I32, I32, I32, I32, I32],
             "mxs_status_str": [ctypes.c_int],
@@ -253,8 +255,8 @@ def index_score_topk(cache: Cache, q_idx, w, topk, block_table=None, scores=None
     return block_table
 
 
-def default_partitions(B, q, topk) -> int:
-    return lib().mxs_default_partitions(B, q, topk)
+def default_partitions(B, q, topk, kv_format="mxfp4") -> int:
+    return lib().mxs_default_partitions_for(B, q, topk, FMT[kv_format])
 
 
 def sparse_split_attn(cache: Cache, q, block_table, sm_scale, num_partitions=0, out=None):
@@ -263,7 +265,7 @@ def sparse_split_attn(cache: Cache, q, block_table, sm_scale, num_partitions=0, 
     B, qr, H, _ = q.shape
     cache.check_batch(B)
     topk = block_table.shape[2]
-    P = num_partitions or default_partitions(B, qr, topk)
+    P = num_partitions or default_partitions(B, qr, topk, cache.kv_format)
     if out is None:
         dev = q.device
         out = (torch.empty((B, qr, H, P), dtype=torch.float32, device=dev),

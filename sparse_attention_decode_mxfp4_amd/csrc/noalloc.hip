@@ -47,8 +47,11 @@ hipError_t scratch_ptr(int dev, void **ptr) {
 extern "C" int decode_step_noalloc(const mxs_step *step, void *stream) {
   char msg[256];
   if (!step) return mxs::api_error(MXS_EINVAL, "step: null");
+  const int32_t P = step->num_partitions != 0
+                        ? step->num_partitions
+                        : mxs_default_partitions_for(step->B, step->q, step->topk, step->cache.kv_format);
   const size_t need = mxs_workspace_bytes(step->B, step->q, step->H, step->H_I, step->topk,
-                                          step->cache.page_table_stride, step->num_partitions);
+                                          step->cache.page_table_stride, P);
   if (need > (size_t)MXS_NOALLOC_SCRATCH_BYTES) {
     snprintf(msg, sizeof msg,
              "decode_step_noalloc: the step needs %zu bytes of workspace, more than the library's "

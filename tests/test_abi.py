@@ -30,7 +30,8 @@ def test_header_declares_the_stages():
     for f in ["mxfp4_row_store", "fp8_row_store", "nvfp4_row_store", "pack_q_e4m3", "index_score", "topk_blocks",
               "index_score_topk", "sparse_split_attn", "lse_merge", "decode_step", "decode_step_reuse",
               "mxs_workspace_bytes",
-              "mxs_default_partitions", "mxs_status_str", "mxs_last_error", "mxs_abi_version",
+              "mxs_default_partitions", "mxs_default_partitions_for", "mxs_status_str", "mxs_last_error",
+              "mxs_abi_version",
               "mxs_score_workspace_bytes", "decode_step_noalloc", "decode_step_reuse_one_launch"]:
         assert f in names, f
     assert set(names) == set(mx.EXPORTS)
@@ -57,6 +58,17 @@ def test_workspace_sizes(L):
     assert L.mxs_default_partitions(16, 8, 32) == 2
     assert L.mxs_default_partitions(32, 8, 32) == 1
     assert L.mxs_default_partitions(64, 16, 64) == 1
+    # FP8 K / V (format 1): two blocks per partition workgroup, ceil(topk / 2), under the same cap;
+    # MXFP4 (0), NVFP4 (2) and unknown formats take ceil(topk / 4)
+    assert L.mxs_default_partitions_for(4, 4, 16, 1) == 8
+    assert [L.mxs_default_partitions_for(4, 4, 16, f) for f in (0, 2, 7)] == [4, 4, 4]
+    assert L.mxs_default_partitions_for(4, 8, 32, 1) == 8          # 256 / 32 rows caps it
+    assert L.mxs_default_partitions_for(1, 1, 1000, 1) == 64
+    assert L.mxs_default_partitions_for(32, 8, 32, 1) == 1
+    # with num_partitions = 0 the workspace fits the larger default (the FP8 workload: P = 8, not 4)
+    rows = 16
+    need8 = rows * 128 * 4 + rows * 16 * 4 + rows * 16 * 128 + 2 * rows * 128 * 4 + rows * 16 * 8 * 128 * 4
+    assert L.mxs_workspace_bytes(4, 4, 16, 4, 16, 128, 0) >= need8
     ws = L.mxs_workspace_bytes(4, 8, 16, 4, 32, 2048, 0)
     rows, P = 32, 8
     need = rows * 2048 * 4 + rows * 32 * 4 + rows * 16 * 128 + 2 * rows * 16 * P * 4 + rows * 16 * P * 128 * 4
@@ -125,7 +137,9 @@ def test_refusal_matrix(L):
 
 def test_decode_step_workspace_check(L):
     s = mx.StepStruct(_cache(), 0, 0, 0, 4096, mx.MXS_F32, 8192, 12288, 2, 8, 16, 4, 32, 0, 0.1, 16384, 0, 0, 0)
-    need = L.mxs_workspace_bytes(2, 8, 16, 4, 32, 16, 0)
+    # the exact need of this MXFP4 step (P = 0 sizes for the larger, FP8, default)
+    need = L.mxs_workspace_bytes(2, 8, 16, 4, 32, 16, L.mxs_default_partitions(2, 8, 32))
+    assert L.mxs_workspace_bytes(2, 8, 16, 4, 32, 16, 0) >= need
     assert L.decode_step(ctypes.byref(s), ctypes.c_void_p(1 << 20), need - 1, None) == mx.MXS_EWORKSPACE
     assert L.decode_step(ctypes.byref(s), None, 0, None) == mx.MXS_EWORKSPACE
     assert L.decode_step(ctypes.byref(s), ctypes.c_void_p((1 << 20) + 16), need, None) == mx.MXS_EINVAL
@@ -142,7 +156,7 @@ def test_decode_step_workspace_check(L):
 def test_decode_step_reuse_rejects_before_launch(L):
     P = ctypes.byref
     s = mx.StepStruct(_cache(idx_pages=0), 0, 0, 0, 4096, mx.MXS_F32, 0, 0, 2, 8, 16, 0, 32, 0, 0.1, 16384, 0, 0, 0)
-    need = L.mxs_workspace_bytes(2, 8, 16, 1, 32, 16, 0)
+    need = L.mxs_workspace_bytes(2, 8, 16, 1, 32, 16, L.mxs_default_partitions(2, 8, 32))
     ws, table = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 16)
     assert L.decode_step_reuse(P(s), None, ws, need, None) == mx.MXS_EINVAL
     assert "block_table" in _err(L)
@@ -167,7 +181,7 @@ def test_decode_step_reuse_one_launch_rejects_like_the_two_launch_step(L):
     (and names itself in the messages)."""
     P = ctypes.byref
     s = mx.StepStruct(_cache(idx_pages=0), 0, 0, 0, 4096, mx.MXS_F32, 0, 0, 2, 8, 16, 0, 32, 0, 0.1, 16384, 0, 0, 0)
-    need = L.mxs_workspace_bytes(2, 8, 16, 1, 32, 16, 0)
+    need = L.mxs_workspace_bytes(2, 8, 16, 1, 32, 16, L.mxs_default_partitions(2, 8, 32))
     ws, table = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 16)
     assert L.decode_step_reuse_one_launch(P(s), None, ws, need, None) == mx.MXS_EINVAL
     assert L.decode_step_reuse_one_launch(P(s), table, ws, need - 1, None) == mx.MXS_EWORKSPACE
