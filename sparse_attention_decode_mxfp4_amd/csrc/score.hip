@@ -16,12 +16,14 @@ template <int FMT, int MT>
 static void launch_mt(const CacheView &c, const uint16_t *q_idx, const float *w, int32_t B, int32_t q,
                       int32_t H_I, float *scores, const StepStore &st, hipStream_t s) {
   const int64_t pages = (int64_t)B * c.stride;
-  if constexpr (FMT == 1) {               // 8.25 KiB chunks: two stages of four waves, two workgroups per CU;
-    // one page per wave below 2048 pages (4 sequences x 128 pages: 5.5 us against 7.2 us for 2 per wave)
+  if constexpr (FMT == 1) {               // 8.25 KiB chunks: two stages per wave
+    // one page per wave below 2048 pages, two waves per workgroup so that the
+    // pages spread over every CU (4 sequences x 128 pages: 4.2 us against 5.1 us
+    // for four waves per workgroup and 7.2 us for two pages per wave)
     if (pages >= 256 * 8)
       launch_shape<FMT, MT, Shape<4, 2, 2>>(c, q_idx, w, B, q, H_I, scores, st, s);
     else
-      launch_shape<FMT, MT, Shape<4, 1, 2>>(c, q_idx, w, B, q, H_I, scores, st, s);
+      launch_shape<FMT, MT, Shape<2, 1, 2>>(c, q_idx, w, B, q, H_I, scores, st, s);
   } else if (pages >= 256 * 16) {         // >= 256 workgroups of 16 pages, two per CU (MXFP4; NVFP4 alike)
     launch_shape<FMT, MT, Shape<4, 4, 2>>(c, q_idx, w, B, q, H_I, scores, st, s);
   } else {
