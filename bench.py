@@ -450,8 +450,11 @@ def main():
                         f"full decode_step ({'eager' if args.eager else 'HIP graph replay'})",
             "B": wl.B, "q": wl.q, "H": wl.H, "H_I": wl.H_I, "topk": wl.topk,
             "context": int(inp.contexts.max()), "cache_replicas": R,
-            "arithmetic": "bf16 MFMA for index scores, QK and PV (e2m1 codes times their block scale, e4m3 codes: "
-                          "widened exactly to bf16), f32 accumulate",
+            "arithmetic": ("f16 MFMA for index scores and QK (NVFP4 codes times their e4m3 block scale, widened "
+                           "exactly to f16; the bf16 query scaled per row into f16), bf16 MFMA for PV, f32 accumulate"
+                           if wl.kv_format == "nvfp4" else
+                           "bf16 MFMA for index scores, QK and PV (e2m1 codes times their block scale, e4m3 codes: "
+                           "widened exactly to bf16), f32 accumulate"),
         },
         "hbm": {"algorithmic_bytes_per_step": ab["total"], "GBps": step_gbps, "peak_GBps": HBM_PEAK_GBPS,
                 "frac": step_gbps / HBM_PEAK_GBPS, "index_bytes": ab["index_pages"],
