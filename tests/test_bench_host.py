@@ -1,7 +1,7 @@
 """Host logic of bench.py, on the CPU: the algorithmic byte count that the
-step's GB/s and the scorer's roofline rest on (SURVEY-style closed forms at
-the headline shape), the HBM traffic lookup keyed to the scorer's sources, and
-the refusal of more than one GPU."""
+step's GB/s and the scorer's roofline rest on (closed forms at the headline
+shape), the HBM traffic lookup keyed to the scorer's sources, and the refusal
+of more than one GPU."""
 import json
 import subprocess
 import sys
