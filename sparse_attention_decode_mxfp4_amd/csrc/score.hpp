@@ -29,6 +29,8 @@
 // in the lane, and the block max is a 16-lane reduction per page.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "rowstore.hpp"
@@ -132,45 +134,62 @@ __device__ __forceinline__ void dma_chunk(uint8_t *stage, const uint8_t *page, i
   }
 }
 
-// B operand (k-step s) of tile nt: the lane's key elements 32 kg + 8 s .. + 7
+// The LDS bytes of tile nt that a lane widens: its codes and scales.
+template <int FMT> struct KeyRaw;
+template <> struct KeyRaw<0> { u32x4 kd; uint32_t sb; };
+template <> struct KeyRaw<1> { u32x4 kd[2]; float ksc; };
+template <> struct KeyRaw<2> { u32x4 kd; uint32_t bs; float ksc; };
+
+template <int FMT>
+__device__ __forceinline__ void key_load(const uint8_t *stage, int nt, int n, int kg, int lane, KeyRaw<FMT> &r) {
+  if constexpr (FMT == 0) {
+    r.kd = *reinterpret_cast<const u32x4 *>(stage + 1024 * nt + 16 * lane);
+    r.sb = stage[Chunk<0>::kCodes + 4 * (16 * nt + n) + kg];
+  } else if constexpr (FMT == 2) {
+    r.kd = *reinterpret_cast<const u32x4 *>(stage + 1024 * nt + 16 * lane);
+    r.bs = *reinterpret_cast<const uint16_t *>(stage + Chunk<2>::kCodes + 8 * (16 * nt + n) + 2 * kg);
+    r.ksc = *reinterpret_cast<const float *>(stage + Chunk<2>::kTok + 4 * (16 * nt + n));
+  } else {
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) r.kd[cc] = *reinterpret_cast<const u32x4 *>(stage + 1024 * (2 * nt + cc) + 16 * lane);
+    r.ksc = *reinterpret_cast<const float *>(stage + Chunk<1>::kCodes + 4 * (16 * nt + n));
+  }
+}
+
+// B operand (k-step s) of a tile: the lane's key elements 32 kg + 8 s .. + 7
 // as bf16 (MXFP4, FP8) or f16 (NVFP4) bits.
 template <int FMT>
-__device__ __forceinline__ void key_operands(const uint8_t *stage, int nt, int n, int kg, int lane, u32x4 Bk[4],
-                                             float &ksc) {
+__device__ __forceinline__ void key_widen(const KeyRaw<FMT> &r, u32x4 Bk[4], float &ksc) {
   if constexpr (FMT == 0) {
-    const u32x4 kd = *reinterpret_cast<const u32x4 *>(stage + 1024 * nt + 16 * lane);
-    const float sf = e8m0_f32(stage[Chunk<0>::kCodes + 4 * (16 * nt + n) + kg]);
+    const float sf = e8m0_f32(r.sb);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       uint32_t w4[4];
-      fp4x8_to_bf16(kd[s], sf, w4);
+      fp4x8_to_bf16(r.kd[s], sf, w4);
       Bk[s] = u32x4{w4[0], w4[1], w4[2], w4[3]};
     }
     ksc = 1.0f;
   } else if constexpr (FMT == 2) {
-    const u32x4 kd = *reinterpret_cast<const u32x4 *>(stage + 1024 * nt + 16 * lane);
-    // the e4m3 scales of blocks 2 kg and 2 kg + 1 of token 16 nt + n, as f16 (exact)
-    const f16x2 bs = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
-        *reinterpret_cast<const uint16_t *>(stage + Chunk<2>::kCodes + 8 * (16 * nt + n) + 2 * kg), 1.0f, false);
+    // the e4m3 scales of blocks 2 kg and 2 kg + 1 of the lane's token, as f16 (exact)
+    const f16x2 bs = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.bs, 1.0f, false);
     const f16x2 s0 = {bs.x, bs.x}, s1 = {bs.y, bs.y};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       uint32_t w4[4];
-      fp4x8_to_f16_nv(kd[s], s < 2 ? s0 : s1, w4);
+      fp4x8_to_f16_nv(r.kd[s], s < 2 ? s0 : s1, w4);
       Bk[s] = u32x4{w4[0], w4[1], w4[2], w4[3]};
     }
-    ksc = *reinterpret_cast<const float *>(stage + Chunk<2>::kTok + 4 * (16 * nt + n));
+    ksc = r.ksc;
   } else {
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
-      const u32x4 kd = *reinterpret_cast<const u32x4 *>(stage + 1024 * (2 * nt + cc) + 16 * lane);
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const uint2 x = e4m3x4_to_bf16(kd[2 * hh]), y = e4m3x4_to_bf16(kd[2 * hh + 1]);
+        const uint2 x = e4m3x4_to_bf16(r.kd[cc][2 * hh]), y = e4m3x4_to_bf16(r.kd[cc][2 * hh + 1]);
         Bk[2 * cc + hh] = u32x4{x.x, x.y, y.x, y.y};
       }
     }
-    ksc = *reinterpret_cast<const float *>(stage + Chunk<1>::kCodes + 4 * (16 * nt + n));
+    ksc = r.ksc;
   }
 }
 
@@ -486,31 +505,56 @@ __device__ __forceinline__ void index_score_wg(const CacheView &c, const uint16_
     const int pos_min = L - q;                        // the first query row's position
 
     // rmax[mt] = max(rmax[mt], the row's score of every token t of chunk (p, h)
-    // with t_lo <= t <= hi[mt]) (all tokens when full)
-    auto chunk_max = [&](const uint8_t *stage, int p, int h, bool full, int t_lo, const int (&hi)[MT],
-                         float (&rmax)[MT]) {
-#pragma unroll 2
-      for (int nt = 0; nt < 4; ++nt) {
-        u32x4 Bk[4];
-        float ksc;
-        key_operands<FMT>(stage, nt, n, kg, lane, Bk, ksc);
-        const int t = p * kTokens + 64 * h + 16 * nt + n;
+    // with t_lo <= t <= hi[mt]) (all tokens when full; always_full, a
+    // compile-time flag, drops the mask altogether). tile_max takes one tile
+    // of 16 tokens (token t in this lane).
+    auto tile_max = [&](auto always_full, const KeyRaw<FMT> &kr, int t, bool full, int t_lo, const int (&hi)[MT],
+                        float (&rmax)[MT]) {
+      u32x4 Bk[4];
+      float ksc;
+      key_widen<FMT>(kr, Bk, ksc);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            if constexpr (FMT == 2)
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, A[mt][s]),
-                                                           __builtin_bit_cast(f16x8, Bk[s]), acc, 0, 0, 0);
-            else
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[mt][s]),
-                                                            __builtin_bit_cast(bf16x8, Bk[s]), acc, 0, 0, 0);
-          }
-          float v = 0.f;
+        for (int s = 0; s < 4; ++s) {
+          if constexpr (FMT == 2)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, A[mt][s]),
+                                                         __builtin_bit_cast(f16x8, Bk[s]), acc, 0, 0, 0);
+          else
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[mt][s]),
+                                                          __builtin_bit_cast(bf16x8, Bk[s]), acc, 0, 0, 0);
+        }
+        float v = 0.f;
 #pragma unroll
-          for (int hd = 0; hd < 4; ++hd) v += wv[mt][hd] * relu1(FMT != 0 ? acc[hd] * ksc : acc[hd]);
+        for (int hd = 0; hd < 4; ++hd) v += wv[mt][hd] * relu1(FMT != 0 ? acc[hd] * ksc : acc[hd]);
+        if constexpr (decltype(always_full)::value)
+          rmax[mt] = fmaxf(rmax[mt], v);
+        else
           rmax[mt] = fmaxf(rmax[mt], (full || (t >= t_lo && t <= hi[mt])) ? v : NEG_INF);
+      }
+    };
+    auto chunk_max = [&](auto always_full, const uint8_t *stage, int p, int h, bool full, int t_lo,
+                         const int (&hi)[MT], float (&rmax)[MT]) {
+      // MXFP4: the chunk's LDS reads all go out first, then its four tiles (one
+      // LDS wait per chunk instead of one per two tiles; 4 sequences x 2048
+      // pages: 17.5 us against 17.9 us per launch, 32 ragged sequences 79.5
+      // against 80.5 us, one session). NVFP4 and FP8 tiles widen with more
+      // registers and keep the two-tile loop (NVFP4 was 0.6 us slower the
+      // other way).
+      if constexpr (FMT == 0) {
+        KeyRaw<FMT> kr[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) key_load<FMT>(stage, nt, n, kg, lane, kr[nt]);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          tile_max(always_full, kr[nt], p * kTokens + 64 * h + 16 * nt + n, full, t_lo, hi, rmax);
+      } else {
+#pragma unroll 2
+        for (int nt = 0; nt < 4; ++nt) {
+          KeyRaw<FMT> kr;
+          key_load<FMT>(stage, nt, n, kg, lane, kr);
+          tile_max(always_full, kr, p * kTokens + 64 * h + 16 * nt + n, full, t_lo, hi, rmax);
         }
       }
     };
@@ -563,7 +607,15 @@ __device__ __forceinline__ void index_score_wg(const CacheView &c, const uint16_
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) rmax[mt] = NEG_INF;
       }
-      chunk_max(stage, p, h, p * kTokens + 64 * h + 63 <= pos_min, INT32_MIN, posw, rmax);
+      // only a wave's first four chunks can hold tokens past the first query
+      // row's position: the last q <= 16 tokens of the context lie in the
+      // last valid page, taken first (chunks 0, 1), or also in the second
+      // half of the page before it (chunk 3). Later chunks are whole, or lie
+      // past the context and are stored as -inf below, so they skip the mask.
+      if (u < 4)
+        chunk_max(std::false_type{}, stage, p, h, p * kTokens + 64 * h + 63 <= pos_min, INT32_MIN, posw, rmax);
+      else
+        chunk_max(std::true_type{}, stage, p, h, true, INT32_MIN, posw, rmax);
       if (h == 1) {
         const bool ok = valid_of(i);
 #pragma unroll

@@ -202,12 +202,17 @@ def test_decode_step_long_with_empty_partitions(mx, b):
     # the same shape at the headline's 8192 pages (the single-launch step's 32-page
     # scoring workgroups have boundaries at 4096-token multiples: the same positions)
     dict(B=4, ctx_rule=("list", (262144, 4100, 8196, 65540)), topk=32),
+    # 16-page workgroups again, the new rows split between two pages of one wave:
+    # 4220..4227 over pages 32 | 33 and 4476..4483 over pages 34 | 35 (the wave's
+    # pages 32..35 taken from its last valid page down, so the earlier page's second
+    # half is the wave's fourth chunk), and 8252..8259 over the two halves of page 64
+    dict(B=4, ctx_rule=("list", (131072, 4228, 4484, 8260)), topk=16),
 ])
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
 def test_decode_step_new_rows_straddle_scorer_workgroups(mx, kw, fmt):
-    """The step's new index rows split between two scorer workgroups, in each
-    of the scorer's launch shapes for MXFP4 pages (NVFP4 pages take the same
-    shapes)."""
+    """The step's new index rows split between two scorer workgroups, or
+    between two pages or chunks of one wave, in each of the scorer's launch
+    shapes for MXFP4 pages (NVFP4 pages take the same shapes)."""
     wl = W.WORKLOADS["mxfp4_65k"].with_(name="straddle", kv_format=fmt, idx_format=fmt,
                                         q_dtype="f32" if fmt == "mxfp4" else "bf16", **kw)
     inp = W.make_inputs(wl)
