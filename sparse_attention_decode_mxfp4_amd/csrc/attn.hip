@@ -497,7 +497,7 @@ template <int NW>
 __device__ __forceinline__ void stage_waves(float (&s_m)[NW][16], float (&s_l)[NW][16],
                                             float (&s_o)[NW][16][kDim + 4], float m_run, float l_run,
                                             const f32x4 O[8]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int n = lane & 15, kg = lane >> 4;
   l_run += u2f(xor_lane<16>(f2u(l_run)));
   l_run += u2f(xor_lane<32>(f2u(l_run)));

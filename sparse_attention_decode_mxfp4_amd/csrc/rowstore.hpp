@@ -184,7 +184,7 @@ __device__ __forceinline__ void reuse_store_wg(const CacheView &c, const float *
                                                int q_dtype, int H, uint8_t *__restrict__ q8,
                                                uint64_t *__restrict__ counters, int q_rows, int row) {
   const int b = row / q_rows, j = row % q_rows;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   if (counters && tid == 0) st_u64<COH>(counters + row, 0ull);
   if (wave < 2) {
     const float *src = wave == 0 ? k_new : v_new;

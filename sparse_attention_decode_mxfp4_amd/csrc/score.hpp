@@ -20,7 +20,7 @@
 // Lane layout (lane = 16 kg + n): for an N-tile of 16 tokens the lane takes
 // the 16 bytes of token n's group kg — one 32-element group and its one scale
 // byte — so a wave's load instruction covers 16 whole token rows (1 KiB,
-// coalesced), copied straight into LDS (see dma_page). The MFMA's K index is
+// coalesced), copied straight into LDS (see dma_chunk). The MFMA's K index is
 // permuted to match: k-step s, lane group kg carries elements 32 kg + 8 s ..
 // 32 kg + 8 s + 7, and the q_idx fragment follows the same permutation (the
 // commit message lays the query fragment out along the 32-element groups as
@@ -108,28 +108,31 @@ __device__ __forceinline__ float max16_dpp(float v) {
 
 template <int FMT>
 __device__ __forceinline__ void dma_chunk(uint8_t *stage, const uint8_t *page, int h, int n, int kg, int lane) {
+  // page and stage are wave-uniform; the per-lane part of each address is a
+  // 32-bit unsigned offset, so the copies take the scalar-base form
+  const uint32_t un = (uint32_t)n, ukg = (uint32_t)kg, ul = (uint32_t)lane, uh = (uint32_t)h;
   if constexpr (FMT == 1) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
-        __builtin_amdgcn_global_load_lds((glb_ptr_t)(page + 128 * (64 * h + 16 * nt + n) + 32 * kg + 16 * cc),
+        __builtin_amdgcn_global_load_lds((glb_ptr_t)(page + (128u * (64u * uh + 16u * nt + un) + 32u * ukg + 16u * cc)),
                                          (lds_ptr_t)(stage + 1024 * (2 * nt + cc)), 16, 0, 0);
   } else {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
-      __builtin_amdgcn_global_load_lds((glb_ptr_t)(page + 64 * (64 * h + 16 * nt + n) + 16 * kg),
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)(page + (64u * (64u * uh + 16u * nt + un) + 16u * ukg)),
                                        (lds_ptr_t)(stage + 1024 * nt), 16, 0, 0);
   }
   if constexpr (FMT == 2) {
 #pragma unroll
     for (int c = 0; c < 2; ++c)
-      __builtin_amdgcn_global_load_lds((glb_ptr_t)(page + kNvBScaleOff + 512 * h + 256 * c + 4 * lane),
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)(page + ((uint32_t)kNvBScaleOff + 512u * uh + 256u * c + 4u * ul)),
                                        (lds_ptr_t)(stage + Chunk<2>::kCodes + 256 * c), 4, 0, 0);
-    __builtin_amdgcn_global_load_lds((glb_ptr_t)(page + kNvTScaleOff + 256 * h + 4 * lane),
+    __builtin_amdgcn_global_load_lds((glb_ptr_t)(page + ((uint32_t)kNvTScaleOff + 256u * uh + 4u * ul)),
                                      (lds_ptr_t)(stage + Chunk<2>::kTok), 4, 0, 0);
   } else {
-    __builtin_amdgcn_global_load_lds((glb_ptr_t)(page + Chunk<FMT>::kScale + 256 * h + 4 * lane),
+    __builtin_amdgcn_global_load_lds((glb_ptr_t)(page + ((uint32_t)Chunk<FMT>::kScale + 256u * uh + 4u * ul)),
                                      (lds_ptr_t)(stage + Chunk<FMT>::kCodes), 4, 0, 0);
   }
 }
@@ -391,7 +394,14 @@ __device__ __forceinline__ void index_score_wg(const CacheView &c, const uint16_
   // take the sequence's pages from the back (d = 0: the last pages, where the
   // step's new rows are, so the wave with the most extra work starts first);
   // the side stores go to the next waves dispatched.
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // The wave index as a wave-uniform (scalar) value: page bases, LDS stage
+  // addresses and the side-work indices then live in SGPRs (4 sequences x
+  // 2048 pages: step 31.8 against 32.2 us; 32 ragged sequences 112.0
+  // against 114.1 us, one session). The two-wave workgroups of small FP8 page
+  // tables measured slower that way (step 16.5 against 16.1 us) and keep the
+  // vector form.
+  const int lane = threadIdx.x & 63;
+  const int wave = NW == 2 ? (int)(threadIdx.x >> 6) : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, kg = lane >> 4;
   const int n_waves = ny * NW, d = gy * NW + wave;
   const int gw = (d + n_waves - 1) % n_waves;        // side-store index: d = 1, 2, ... first

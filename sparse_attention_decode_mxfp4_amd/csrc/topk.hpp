@@ -114,7 +114,7 @@ __device__ __forceinline__ uint32_t wg_topk(const float (&v)[ITEMS], int n_cand,
                                             int &n_sel) {
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   constexpr int NT = 64 * NW;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (n_cand <= topk) {                      // every candidate is selected
     n_sel = n_cand;
     return (uint32_t)lane;
