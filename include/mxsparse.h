@@ -200,14 +200,15 @@ int sparse_split_attn(const mxs_cache *cache, const void *q, int32_t q_dtype,
                       const int32_t *block_table, int32_t B, int32_t q_rows, int32_t H,
                       int32_t topk, int32_t num_partitions, float sm_scale, float *sp_m,
                       float *sp_l, float *sp_o, void *stream);
-/* The partition count the library takes for num_partitions = 0 over K / V
- * pages of format kv_format: min(ceil(topk / 4), max(1, 256 / (B q_rows))),
- * clamped to 1..64 — one block per wave of a 4-wave workgroup, but no more
- * workgroups than MI355X has CUs once the rows alone fill it — with
- * ceil(topk / 2) in place of ceil(topk / 4) for FP8 K / V, whose pages are
- * twice as large (two blocks per workgroup). A choice of this library; the
- * pages fix none. Unknown formats take the MXFP4 rule.
- * mxs_default_partitions: the same for MXFP4 (and NVFP4) K / V. */
+/* The partition count the library takes for num_partitions = 0, the same
+ * for every K / V format: P = min(ceil(topk / 4), cap) with cap = max(1, 256 /
+ * (B q_rows)) — one block per wave of a 4-wave workgroup, but no more
+ * workgroups than MI355X has CUs once the rows alone fill it; if P B q_rows
+ * is then below 256, min(ceil(topk / 2), cap) instead (two blocks per
+ * workgroup, which its waves take as half blocks); clamped to 1..64. A
+ * choice of this library; the pages fix none. kv_format is not consulted
+ * (kept so that callers can state the format).
+ * mxs_default_partitions: the same. */
 int mxs_default_partitions_for(int32_t B, int32_t q_rows, int32_t topk, int32_t kv_format);
 int mxs_default_partitions(int32_t B, int32_t q_rows, int32_t topk);
 
@@ -248,8 +249,8 @@ typedef struct {
  * initialization and are scratch after the call (it holds the per-row merge
  * counters, cleared by the first launch), so two calls in flight at once must
  * not share one. mxs_workspace_bytes with num_partitions = 0 sizes for the
- * larger default over the formats (mxs_default_partitions_for), enough for
- * any cache format. */
+ * default partition count (mxs_default_partitions), which is the same for
+ * every cache format. */
 int decode_step(const mxs_step *step, void *ws, size_t ws_bytes, void *stream);
 size_t mxs_workspace_bytes(int32_t B, int32_t q, int32_t H, int32_t H_I, int32_t topk,
                            int32_t page_table_stride, int32_t num_partitions);

@@ -101,27 +101,27 @@ mxs::CacheView view(const mxs_cache *c) {
 
 size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Partitions per query row when the caller leaves the choice to the library:
-// one block per wave of a 4-wave partition workgroup (ceil(topk / 4)); with
-// FP8 K / V, whose pages are twice as large, two blocks per workgroup
-// (ceil(topk / 2): the FP8 workload, 4 x 4 rows and k = 16, measured 16.9 us
-// per step at P = 8 against 18.1 at P = 4, where each CU streams 135 KB of
-// K / V pages); but no more than it takes to give each of MI355X's 256 CUs one
-// workgroup. Every workgroup runs the same dependent chain (selection, block
-// loads, exchange of partials), so when the rows alone fill the GPU, fewer and
-// longer partitions beat several rounds of short ones.
+// Partitions per query row when the caller leaves the choice to the library,
+// for every K / V format: one block per wave of a 4-wave partition workgroup
+// (ceil(topk / 4)), but no more than it takes to give each of MI355X's 256
+// CUs one workgroup. If that leaves CUs without a workgroup, two blocks per
+// workgroup instead (ceil(topk / 2), within the same cap): its 4 waves then
+// take half blocks (the attention kernels' step_tiles), so every wave still
+// works and twice as many workgroups share the rows. Every workgroup runs the
+// same dependent chain (selection, block loads, exchange of partials), so
+// when the rows alone fill the GPU, fewer and longer partitions beat several
+// rounds of short ones. Measured on MI355X (step): top-k 16 over 4 x 8 MXFP4
+// rows 18.1 us at P = 8 (half blocks) against 18.4 at P = 4, over NVFP4 rows
+// 19.1 against 20.3, over 4 x 4 FP8 rows 15.2 against 16.2 with whole blocks
+// at the same P = 8; top-k 32 over 4 x 8 rows keeps P = 8 with whole blocks
+// (32.5 us; 35.0 at P = 16 with half blocks).
 constexpr int64_t kTargetWorkgroups = 256;
-int default_partitions(int32_t B, int32_t q_rows, int32_t topk, int32_t kv_format = MXS_FMT_MXFP4) {
+int default_partitions(int32_t B, int32_t q_rows, int32_t topk) {
   const int64_t rows = (int64_t)B * q_rows;
-  const int64_t per = kv_format == MXS_FMT_FP8 ? 2 : 4;          // blocks per partition workgroup
-  int64_t p = (topk + per - 1) / per;
-  if (rows > 0) p = std::min<int64_t>(p, std::max<int64_t>(1, kTargetWorkgroups / rows));
+  const int64_t cap = rows > 0 ? std::max<int64_t>(1, kTargetWorkgroups / rows) : MXS_MAX_PARTITIONS;
+  int64_t p = std::min<int64_t>((topk + 3) / 4, cap);
+  if (p * rows < kTargetWorkgroups) p = std::min<int64_t>((topk + 1) / 2, cap);
   return (int)std::max<int64_t>(1, std::min<int64_t>(p, MXS_MAX_PARTITIONS));
-}
-// the default the workspace query sizes for when the format is not given: the
-// largest over the formats (FP8's)
-int default_partitions_any(int32_t B, int32_t q_rows, int32_t topk) {
-  return std::max(default_partitions(B, q_rows, topk, MXS_FMT_MXFP4), default_partitions(B, q_rows, topk, MXS_FMT_FP8));
 }
 
 // workspace segments of decode_step, in order
@@ -270,7 +270,8 @@ int mxs_default_partitions(int32_t B, int32_t q_rows, int32_t topk) {
 }
 
 int mxs_default_partitions_for(int32_t B, int32_t q_rows, int32_t topk, int32_t kv_format) {
-  return default_partitions(B, q_rows, topk, kv_format);
+  (void)kv_format;                                 // the same rule for every format
+  return default_partitions(B, q_rows, topk);
 }
 
 static int check_attn_args(const mxs_cache *cache, const void *q, int32_t q_dtype, const int32_t *block_table,
@@ -296,7 +297,7 @@ int sparse_split_attn(const mxs_cache *cache, const void *q, int32_t q_dtype, co
                       int32_t q_rows, int32_t H, int32_t topk, int32_t num_partitions, float sm_scale, float *sp_m,
                       float *sp_l, float *sp_o, void *stream) {
   REQ(cache, MXS_EINVAL, "cache: null");
-  const int32_t P = num_partitions == 0 ? default_partitions(B, q_rows, topk, cache->kv_format) : num_partitions;
+  const int32_t P = num_partitions == 0 ? default_partitions(B, q_rows, topk) : num_partitions;
   if (int r = check_attn_args(cache, q, q_dtype, block_table, B, q_rows, H, topk, P, sm_scale)) return r;
   REQ(sp_m && sp_l && sp_o, MXS_EINVAL, "sp_m / sp_l / sp_o: null");
   REQ(aligned(sp_m, 4) && aligned(sp_l, 4) && aligned(sp_o, 16), MXS_EINVAL, "sp_m / sp_l / sp_o: misaligned");
@@ -333,7 +334,7 @@ size_t mxs_workspace_bytes(int32_t B, int32_t q, int32_t H, int32_t H_I, int32_t
                            int32_t num_partitions) {
   (void)H_I;
   if (B < 0 || q < 0 || H < 0 || topk < 0 || page_table_stride < 0) return 0;
-  const int32_t P = num_partitions == 0 ? default_partitions_any(B, q, topk) : num_partitions;
+  const int32_t P = num_partitions == 0 ? default_partitions(B, q, topk) : num_partitions;
   return step_ws(B, q, H, topk, page_table_stride, P).total;
 }
 
@@ -356,7 +357,7 @@ static int step_entry(const mxs_step *a, void *ws, size_t ws_bytes, void *stream
   if (int r = check_topk(a->topk)) return r;
   if (a->B == 0) return ok();                      // an empty batch: nothing to do
   const int32_t P =
-      a->num_partitions == 0 ? default_partitions(a->B, a->q, a->topk, a->cache.kv_format) : a->num_partitions;
+      a->num_partitions == 0 ? default_partitions(a->B, a->q, a->topk) : a->num_partitions;
   const bool mx = cache->kv_format == MXS_FMT_MXFP4;
   if (mx)
     REQ(a->q_dtype == MXS_F32 || a->q_dtype == MXS_BF16, MXS_EUNSUPPORTED,
@@ -473,7 +474,7 @@ static int reuse_entry(const mxs_step *a, const int32_t *block_table, void *ws, 
   if (int r = check_topk(a->topk)) return r;
   if (a->B == 0) return ok();                      // an empty batch: nothing to do
   const int32_t P =
-      a->num_partitions == 0 ? default_partitions(a->B, a->q, a->topk, a->cache.kv_format) : a->num_partitions;
+      a->num_partitions == 0 ? default_partitions(a->B, a->q, a->topk) : a->num_partitions;
   const bool mx = cache->kv_format == MXS_FMT_MXFP4;
   if (mx)
     REQ(a->q_dtype == MXS_F32 || a->q_dtype == MXS_BF16, MXS_EUNSUPPORTED,

@@ -11,11 +11,12 @@
 // * Workgroup = (partition p, query row j, sequence b), 4 waves. Partition p
 //   owns block-table slots [p c, min((p+1) c, topk)), c = ceil(topk / P); wave
 //   w takes every 4th of them, keeps an online softmax (m, l, O) for the 16
-//   heads, and the 4 waves merge through LDS into one partial. The block code
-//   takes the wave's token range as a parameter; only whole blocks are built.
-//   (Half blocks for 8-wave workgroups, waves in pairs, measured slower on
-//   MI355X: the 8-wave selection and merge lose more at their barriers than
-//   the halved block work gains.)
+//   heads, and the 4 waves merge through LDS into one partial. A wave's token
+//   range is a whole block, or half a block when a partition owns at most two
+//   blocks (step_tiles: waves in pairs, so that all 4 waves work; with whole
+//   blocks two of them would idle). (Half blocks for 8-wave workgroups
+//   measured slower on MI355X: the 8-wave selection and merge lose more at
+//   their barriers than the halved block work gains.)
 // * QK: D[token][head] = K[token][:] . q[head][:] on v_mfma_f32_16x16x32_bf16.
 //   Lane 16 kg + n loads token n's group kg — 16 bytes and one scale byte, the
 //   same coalesced pattern as the index scorer — and widens it to bf16 with
@@ -56,7 +57,16 @@ namespace mxs {
 
 constexpr int kAttnWaves = 4;    // the stand-alone split stage
 constexpr int kStepWaves = 4;    // the decode step's attention launch
-constexpr int kStepTiles = 8;    // 16-token tiles per wave and block (8: whole blocks)
+
+// 16-token tiles per wave's token range in the attention launches: whole
+// blocks (8), or half blocks (4) when a partition owns at most two blocks, so
+// that its 4 waves all work (two waves per block). Measured on MI355X at the
+// default partition counts (step, same session): top-k 16 over 4 x 4 FP8 rows
+// 15.2 against 16.2 us; top-k 16 over 4 x 8 NVFP4 rows (8 partitions) 19.1
+// against 20.3 us with whole blocks at 4 partitions; the MXFP4 65K workload
+// 18.1 against 18.4 us. With more than two blocks per partition whole blocks
+// win (top-k 32 over 4 x 8 rows: 32.5 us against 33.2 us for half blocks).
+constexpr int step_tiles(int topk, int P) { return (topk + P - 1) / P <= 2 ? 4 : 8; }
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -609,7 +619,7 @@ __device__ __forceinline__ void write_row(float (&s_m)[NW][16], float (&s_l)[NW]
   }
 }
 
-template <int FMT>
+template <int FMT, int TILES>
 __global__ __launch_bounds__(256) void k_split_attn(CacheView c, const void *__restrict__ qv,
                                                     const int32_t *__restrict__ block_table,
                                                     int32_t q_rows, int32_t H, int32_t topk, int32_t P,
@@ -631,7 +641,7 @@ __global__ __launch_bounds__(256) void k_split_attn(CacheView c, const void *__r
   f32x4 O[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  attend_slots<FMT, kAttnWaves, 8>(
+  attend_slots<FMT, kAttnWaves, TILES>(
       c, slot0, slot1, pos, qr, H, sm_scale * kLog2e, m_run, l_run, O, n, kg,
       [&](int slot) {
         const int blk = __builtin_amdgcn_readfirstlane(block_table[(int64_t)row * topk + slot]);
@@ -709,7 +719,7 @@ __device__ __forceinline__ void reuse_row_done(const StepWait &sw, int b, int q_
 // holds no line that was not fetched in this launch, and every wave that
 // reads those pages has waited first.) q_dtype: the caller's query dtype
 // (kOneLaunchReuse with MXFP4 K / V only).
-template <int FMT, int ITEMS, bool SELECT, int MODE>
+template <int FMT, int ITEMS, bool SELECT, int MODE, int TILES>
 __device__ __forceinline__ void step_attn_wg(const CacheView &c, const float *__restrict__ scores,
                                              const void *__restrict__ qv, int32_t q_rows, int32_t H, int32_t topk,
                                              int32_t P, float sm_scale, int32_t *__restrict__ block_table,
@@ -802,7 +812,7 @@ __device__ __forceinline__ void step_attn_wg(const CacheView &c, const float *__
     // a range reaching the step's new positions (L - q_rows ..) waits for the
     // sequence's store workgroups (bounded)
     const int new0 = L - q_rows;
-    attend_slots<FMT, kStepWaves, kStepTiles>(
+    attend_slots<FMT, kStepWaves, TILES>(
         c, slot0, slot1, pos, qr, H, sm_scale * kLog2e, m_run, l_run, O, n, kg, blk_of, phys_of, [&](int t_last) {
           if (t_last < new0) return;
           uint32_t spins = 0;
@@ -812,7 +822,7 @@ __device__ __forceinline__ void step_attn_wg(const CacheView &c, const float *__
             __builtin_amdgcn_s_sleep(2);
         });
   } else {
-    attend_slots<FMT, kStepWaves, kStepTiles>(c, slot0, slot1, pos, qr, H, sm_scale * kLog2e, m_run, l_run, O, n, kg,
+    attend_slots<FMT, kStepWaves, TILES>(c, slot0, slot1, pos, qr, H, sm_scale * kLog2e, m_run, l_run, O, n, kg,
                                               blk_of, phys_of);
   }
   if (P == 1) {                                     // the row is this workgroup's alone: no exchange
@@ -869,7 +879,7 @@ __device__ __forceinline__ int xcd_item(int lin, int n) {
   return (n & 7) == 0 ? (lin & 7) * (n >> 3) + (lin >> 3) : lin;
 }
 
-template <int FMT, int ITEMS, bool SELECT>
+template <int FMT, int ITEMS, bool SELECT, int TILES>
 __global__ __launch_bounds__(64 * kStepWaves) void k_select_attn(CacheView c, const float *__restrict__ scores,
                                                      const void *__restrict__ qv, int32_t q_rows, int32_t H,
                                                      int32_t topk, int32_t P, float sm_scale,
@@ -878,8 +888,9 @@ __global__ __launch_bounds__(64 * kStepWaves) void k_select_attn(CacheView c, co
                                                      FusedMerge fm) {
   __shared__ StepAttnSmem<ITEMS, SELECT> sm;
   const int r = xcd_item(blockIdx.x, gridDim.x);   // item r: partition r % P, row (r / P) % q_rows, sequence
-  step_attn_wg<FMT, ITEMS, SELECT, kTwoLaunch>(c, scores, qv, q_rows, H, topk, P, sm_scale, block_table, sp_m, sp_l,
-                                               sp_o, fm, StepWait{}, r % P, (r / P) % q_rows, r / (P * q_rows), sm);
+  step_attn_wg<FMT, ITEMS, SELECT, kTwoLaunch, TILES>(c, scores, qv, q_rows, H, topk, P, sm_scale, block_table, sp_m,
+                                                      sp_l, sp_o, fm, StepWait{}, r % P, (r / P) % q_rows,
+                                                      r / (P * q_rows), sm);
 }
 
 // ---------------------------------------------------------------- the step as one launch
@@ -902,7 +913,7 @@ constexpr int kStepLds = kScoreLds<MT, 0, 4, 3> > (int)sizeof(StepAttnSmem<ITEMS
                              ? kScoreLds<MT, 0, 4, 3>
                              : (int)sizeof(StepAttnSmem<ITEMS, true>);
 
-template <int MT, int ITEMS>
+template <int MT, int ITEMS, int TILES>
 __global__ __launch_bounds__(64 * kStepWaves) void k_decode_step(
     CacheView c, const uint16_t *__restrict__ q_idx, const float *__restrict__ w, int32_t q, int32_t H_I,
     float *__restrict__ scores, StepStore st, int32_t B, int32_t ny, int32_t H, int32_t topk, int32_t P,
@@ -923,8 +934,9 @@ __global__ __launch_bounds__(64 * kStepWaves) void k_decode_step(
   }
   const int a = xcd_item((int)blockIdx.x - n_score, (int)gridDim.x - n_score);   // XCD runs when 8 divides n_score
   const int p = a % P, j = (a / P) % q, b = a / (P * q);
-  step_attn_wg<0, ITEMS, true, kOneLaunchStep>(c, scores, st.q8, q, H, topk, P, sm_scale, block_table, sp_m, sp_l,
-                                               sp_o, fm, sw, p, j, b, *reinterpret_cast<StepAttnSmem<ITEMS, true> *>(lds));
+  step_attn_wg<0, ITEMS, true, kOneLaunchStep, TILES>(c, scores, st.q8, q, H, topk, P, sm_scale, block_table, sp_m,
+                                                      sp_l, sp_o, fm, sw, p, j, b,
+                                                      *reinterpret_cast<StepAttnSmem<ITEMS, true> *>(lds));
 }
 
 // ---------------------------------------------------------------- the reuse step as one launch
@@ -938,7 +950,7 @@ __global__ __launch_bounds__(64 * kStepWaves) void k_decode_step(
 // dispatched first (increasing ids per XCD), so every wait ends; it is also
 // bounded (kWaitSpins). The merge counters and the sequence counters
 // (seq_cnt) must be zero before the first launch and are left zero.
-template <int FMT, int ITEMS>
+template <int FMT, int ITEMS, int TILES>
 __global__ __launch_bounds__(64 * kStepWaves) void k_reuse_step(
     CacheView c, const float *__restrict__ k_new, const float *__restrict__ v_new, const void *__restrict__ q_src,
     int32_t q_dtype, int32_t q_rows, int32_t H, int32_t topk, int32_t P, float sm_scale,
@@ -957,9 +969,9 @@ __global__ __launch_bounds__(64 * kStepWaves) void k_reuse_step(
   }
   const int a = xcd_item((int)blockIdx.x - n_store, (int)gridDim.x - n_store);
   const int p = a % P, j = (a / P) % q_rows, b = a / (P * q_rows);
-  step_attn_wg<FMT, ITEMS, false, kOneLaunchReuse>(c, nullptr, q_src, q_rows, H, topk, P, sm_scale,
-                                                   const_cast<int32_t *>(block_table), sp_m, sp_l, sp_o, fm, sw, p, j,
-                                                   b, sm, q_dtype);
+  step_attn_wg<FMT, ITEMS, false, kOneLaunchReuse, TILES>(c, nullptr, q_src, q_rows, H, topk, P, sm_scale,
+                                                          const_cast<int32_t *>(block_table), sp_m, sp_l, sp_o, fm,
+                                                          sw, p, j, b, sm, q_dtype);
 }
 
 hipError_t launch_reuse_step(const CacheView &c, const float *k_new, const float *v_new, const void *q, int q_dtype,
@@ -973,9 +985,14 @@ hipError_t launch_reuse_step(const CacheView &c, const float *k_new, const float
   sw.n_score = (uint32_t)q_rows;                   // store workgroups per sequence
   const int n_store = B * q_rows;
   const dim3 grid((unsigned)(n_store + B * q_rows * P)), block(NT);
-#define MXS_REUSE(F, I)                                                                                         \
-  hipLaunchKernelGGL((k_reuse_step<F, I>), grid, block, 0, s, c, k_new, v_new, q, q_dtype, q_rows, H, topk, P,   \
+#define MXS_REUSE_T(F, I, T)                                                                                     \
+  hipLaunchKernelGGL((k_reuse_step<F, I, T>), grid, block, 0, s, c, k_new, v_new, q, q_dtype, q_rows, H, topk, P, \
                      sm_scale, block_table, sp_m, sp_l, sp_o, fm, sw, n_store)
+#define MXS_REUSE(F, I)                                            \
+  do {                                                             \
+    if (step_tiles(topk, P) == 4) MXS_REUSE_T(F, I, 4);            \
+    else MXS_REUSE_T(F, I, 8);                                     \
+  } while (0)
 #define MXS_REUSE_FMT(F)                            \
   if (c.stride <= NT * 2) MXS_REUSE(F, 2);          \
   else if (c.stride <= NT * 8) MXS_REUSE(F, 8);     \
@@ -989,6 +1006,7 @@ hipError_t launch_reuse_step(const CacheView &c, const float *k_new, const float
   }
 #undef MXS_REUSE_FMT
 #undef MXS_REUSE
+#undef MXS_REUSE_T
   return hipGetLastError();
 }
 
@@ -1007,13 +1025,19 @@ static void launch_step_mt(const CacheView &c, const uint16_t *q_idx, const floa
   sw.seq_cnt = seq_cnt;
   sw.n_score = (uint32_t)ny;
   const dim3 grid((unsigned)(B * ny + B * q * P)), block(NT);
-#define MXS_STEP(I)                                                                                           \
-  hipLaunchKernelGGL((k_decode_step<MT, I>), grid, block, 0, s, c, q_idx, w, q, H_I, scores, st, B, ny, H, topk, \
-                     P, sm_scale, block_table, sp_m, sp_l, sp_o, fm, sw)
+#define MXS_STEP_T(I, T)                                                                                         \
+  hipLaunchKernelGGL((k_decode_step<MT, I, T>), grid, block, 0, s, c, q_idx, w, q, H_I, scores, st, B, ny, H,      \
+                     topk, P, sm_scale, block_table, sp_m, sp_l, sp_o, fm, sw)
+#define MXS_STEP(I)                                                \
+  do {                                                             \
+    if (step_tiles(topk, P) == 4) MXS_STEP_T(I, 4);                \
+    else MXS_STEP_T(I, 8);                                         \
+  } while (0)
   if (c.stride <= NT * 2) MXS_STEP(2);
   else if (c.stride <= NT * 8) MXS_STEP(8);
   else MXS_STEP(32);
 #undef MXS_STEP
+#undef MXS_STEP_T
 }
 
 hipError_t launch_decode_step(const CacheView &c, const uint16_t *q_idx, const float *w, int32_t B, int32_t q,
@@ -1036,15 +1060,18 @@ hipError_t launch_split_attn(const CacheView &c, const void *q, int q_dtype, con
   (void)q_dtype;
   if (B * q_rows == 0) return hipSuccess;
   const dim3 grid((unsigned)P, (unsigned)q_rows, (unsigned)B);
-  if (c.kv_format == 0)
-    hipLaunchKernelGGL(k_split_attn<0>, grid, dim3(256), 0, s, c, q, block_table, q_rows, H, topk, P, sm_scale,
-                       sp_m, sp_l, sp_o);
-  else if (c.kv_format == 1)
-    hipLaunchKernelGGL(k_split_attn<1>, grid, dim3(256), 0, s, c, q, block_table, q_rows, H, topk, P, sm_scale,
-                       sp_m, sp_l, sp_o);
-  else
-    hipLaunchKernelGGL(k_split_attn<2>, grid, dim3(256), 0, s, c, q, block_table, q_rows, H, topk, P, sm_scale,
-                       sp_m, sp_l, sp_o);
+#define MXS_SPLIT(F, T)                                                                                     \
+  hipLaunchKernelGGL((k_split_attn<F, T>), grid, dim3(256), 0, s, c, q, block_table, q_rows, H, topk, P,   \
+                     sm_scale, sp_m, sp_l, sp_o)
+  const bool half = step_tiles(topk, P) == 4;
+  if (c.kv_format == 0) {
+    if (half) MXS_SPLIT(0, 4); else MXS_SPLIT(0, 8);
+  } else if (c.kv_format == 1) {
+    if (half) MXS_SPLIT(1, 4); else MXS_SPLIT(1, 8);
+  } else {
+    if (half) MXS_SPLIT(2, 4); else MXS_SPLIT(2, 8);
+  }
+#undef MXS_SPLIT
   return hipGetLastError();
 }
 
@@ -1054,9 +1081,14 @@ static void launch_attn_items(const CacheView &c, const float *scores, const voi
                               float *sp_l, float *sp_o, const FusedMerge &fm, hipStream_t s) {
   constexpr int NT = 64 * kStepWaves;
   const dim3 grid((unsigned)(P * q_rows * B)), block(NT);
-#define MXS_SELECT_ATTN(F, I)                                                                                   \
-  hipLaunchKernelGGL((k_select_attn<F, I, SELECT>), grid, block, 0, s, c, scores, q, q_rows, H, topk, P,       \
+#define MXS_SELECT_ATTN_T(F, I, T)                                                                               \
+  hipLaunchKernelGGL((k_select_attn<F, I, SELECT, T>), grid, block, 0, s, c, scores, q, q_rows, H, topk, P,     \
                      sm_scale, block_table, sp_m, sp_l, sp_o, fm)
+#define MXS_SELECT_ATTN(F, I)                                      \
+  do {                                                             \
+    if (step_tiles(topk, P) == 4) MXS_SELECT_ATTN_T(F, I, 4);      \
+    else MXS_SELECT_ATTN_T(F, I, 8);                               \
+  } while (0)
   static_assert(NT * 32 >= MXS_MAX_PAGES_PER_SEQ, "candidates per thread");
   if (c.kv_format == 0) {
     if (c.stride <= NT * 2) MXS_SELECT_ATTN(0, 2);
@@ -1072,6 +1104,7 @@ static void launch_attn_items(const CacheView &c, const float *scores, const voi
     else MXS_SELECT_ATTN(2, 32);
   }
 #undef MXS_SELECT_ATTN
+#undef MXS_SELECT_ATTN_T
 }
 
 hipError_t launch_select_attn(const CacheView &c, const float *scores, const void *q, int32_t B, int32_t q_rows,

@@ -50,22 +50,22 @@ def test_version_and_status_strings(L):
 
 
 def test_workspace_sizes(L):
-    assert L.mxs_default_partitions(4, 8, 32) == 8
-    assert L.mxs_default_partitions(1, 1, 4) == 1
+    assert L.mxs_default_partitions(4, 8, 32) == 8          # ceil(32 / 4) x 32 rows = 256 workgroups
     assert L.mxs_default_partitions(1, 1, 1000) == 64
     # once the rows alone fill the GPU's 256 CUs, fewer (longer) partitions
-    assert L.mxs_default_partitions(4, 4, 16) == 4
     assert L.mxs_default_partitions(16, 8, 32) == 2
     assert L.mxs_default_partitions(32, 8, 32) == 1
     assert L.mxs_default_partitions(64, 16, 64) == 1
-    # FP8 K / V (format 1): two blocks per partition workgroup, ceil(topk / 2), under the same cap;
-    # MXFP4 (0), NVFP4 (2) and unknown formats take ceil(topk / 4)
-    assert L.mxs_default_partitions_for(4, 4, 16, 1) == 8
-    assert [L.mxs_default_partitions_for(4, 4, 16, f) for f in (0, 2, 7)] == [4, 4, 4]
-    assert L.mxs_default_partitions_for(4, 8, 32, 1) == 8          # 256 / 32 rows caps it
-    assert L.mxs_default_partitions_for(1, 1, 1000, 1) == 64
-    assert L.mxs_default_partitions_for(32, 8, 32, 1) == 1
-    # with num_partitions = 0 the workspace fits the larger default (the FP8 workload: P = 8, not 4)
+    # ceil(topk / 4) leaves CUs without a workgroup: two blocks per workgroup, ceil(topk / 2), same cap
+    assert L.mxs_default_partitions(1, 1, 4) == 2
+    assert L.mxs_default_partitions(4, 4, 16) == 8           # 16 rows: 4 -> 8 (cap 16)
+    assert L.mxs_default_partitions(4, 8, 16) == 8           # 32 rows: 4 -> 8 (cap 8)
+    assert L.mxs_default_partitions(4, 8, 20) == 8           # ceil(20 / 2) = 10, capped at 8
+    assert L.mxs_default_partitions(8, 8, 16) == 4           # 64 rows: 4 x 64 = 256 already
+    # the same rule for every format
+    assert [L.mxs_default_partitions_for(4, 4, 16, f) for f in (0, 1, 2, 7)] == [8, 8, 8, 8]
+    assert [L.mxs_default_partitions_for(32, 8, 32, f) for f in (0, 1, 2)] == [1, 1, 1]
+    # with num_partitions = 0 the workspace fits the default (the FP8 workload: P = 8)
     rows = 16
     need8 = rows * 128 * 4 + rows * 16 * 4 + rows * 16 * 128 + 2 * rows * 128 * 4 + rows * 16 * 8 * 128 * 4
     assert L.mxs_workspace_bytes(4, 4, 16, 4, 16, 128, 0) >= need8
