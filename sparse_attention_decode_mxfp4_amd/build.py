@@ -5,6 +5,9 @@
 Every HIP source is compiled with hipcc for gfx950 only. Packed fp32 VALU
 instructions are disabled (-packed-fp32-ops) and fp32 division and square
 root are correctly rounded (the FP8 row store divides by its per-token scale).
+The target feature reaches the host pass too, which warns that it does not
+know it and ignores it: clang's -Xarch_device passes no option that takes an
+argument, so -Xclang -target-feature cannot be limited to the device pass.
 MFMA results go to VGPRs (-amdgpu-mfma-vgpr-form): the kernels read every
 accumulator with VALU code, which AGPR results would first have to copy out.
 """
