@@ -17,9 +17,10 @@ pools. Inputs are resident in HBM before timing starts, and the GPU has been kep
 busy with untimed step replays for --settle-ms of wall time (it lowers its
 clocks when idle; each later kernel timing is preceded by its own shorter
 settle), then the W warmup steps run. Each timed step runs on the
-next of R cache replicas (R * ~90 MB touched per step > the 256 MB Infinity
-Cache), so the index scan streams from HBM, not from the MALL; the one-replica
-(warm) number is reported separately.
+next of R cache replicas, R at least --replicas (6) and enough that R steps
+touch 512 MB, twice the 256 MB Infinity Cache (the 256K workload: 6 x ~88 MB),
+so that every workload's scan streams from HBM, as a model's layers would, not
+from the MALL; the one-replica (warm) number is reported separately.
 
 Prints one JSON line (rank 0): the metric (query rows/s), the whole step's
 algorithmic HBM bytes and GB/s, the roofline of the dominant kernel (the index
@@ -42,6 +43,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+# bytes the R replicas' steps must touch together: twice the 256 MB Infinity Cache
+ROTATION_BYTES = 512_000_000
 PAGE_MX = 8704
 # page bytes and bytes of one stored 128-element row, per cache format
 PAGE_BYTES = {"mxfp4": 8704, "fp8": 16896, "nvfp4": 9728}
@@ -239,20 +242,34 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] filled {wl.name} caches in {time.perf_counter() - t_setup:.1f} s")
     t = WG.step_tensors(inp)
-    R = max(1, args.replicas)
-    replicas = [pools0] + [{s: p.clone() for s, p in pools0.items()} for _ in range(R - 1)]
-    # the replicas share one page table and context-length vector, as the layers
-    # of a decode step share the sequences' block table; each has its own pools
-    c0 = WG.make_cache(inp, replicas[0])
-    caches = [c0] + [WG.make_cache(inp, p, table=c0.page_table, ctx=c0.context_lens) for p in replicas[1:]]
-    tables = [torch.empty((wl.B, wl.q, wl.topk), dtype=torch.int32, device="cuda") for _ in range(R)]
-    steps = [mx.DecodeStep(c, t["query"], t["q_idx"], t["w"], wl.topk, wl.sm_scale, k_new=t.get("k_new"),
-                           v_new=t.get("v_new"), idx_new=t.get("idx_new"), block_table_out=tb)
-             for c, tb in zip(caches, tables)]
+
+    def make_step(c, tb):
+        return mx.DecodeStep(c, t["query"], t["q_idx"], t["w"], wl.topk, wl.sm_scale, k_new=t.get("k_new"),
+                             v_new=t.get("v_new"), idx_new=t.get("idx_new"), block_table_out=tb)
+
+    # replica 0 first: one step gives the block table, hence the bytes a step
+    # touches; then R replicas, at least --replicas and enough that R steps
+    # touch ROTATION_BYTES, so that no replica is still in the caches when its
+    # turn comes again (a step rewrites the same new rows each time, so the
+    # copies of replica 0 hold what their own first step would leave). The
+    # replicas share one page table and context-length vector, as the layers of
+    # a decode step share the sequences' block table; each has its own pools.
+    c0 = WG.make_cache(inp, pools0)
+    tables = [torch.empty((wl.B, wl.q, wl.topk), dtype=torch.int32, device="cuda")]
+    steps = [make_step(c0, tables[0])]
+    steps[0].run()
+    torch.cuda.synchronize()
+    ab = algorithmic_bytes(inp, tables[0].cpu().numpy())
+    R = max(1, args.replicas, -(-ROTATION_BYTES // max(1, ab["total"])))
+    caches = [c0]
+    for _ in range(R - 1):
+        pools = {s_: p.clone() for s_, p in pools0.items()}
+        caches.append(WG.make_cache(inp, pools, table=c0.page_table, ctx=c0.context_lens))
+        tables.append(torch.empty((wl.B, wl.q, wl.topk), dtype=torch.int32, device="cuda"))
+        steps.append(make_step(caches[-1], tables[-1]))
     for s in steps:
         s.run()
     torch.cuda.synchronize()
-    ab = algorithmic_bytes(inp, tables[0].cpu().numpy())
 
     # ---- the timed region: exactly K steps, rotating replicas (step i runs on
     # replica i % R, like the layers of one decode step, each with its own

@@ -2,8 +2,9 @@
 // sequence read once, in page-table order, with plain 16-byte loads folded
 // into one word per workgroup. Nothing is widened, multiplied or written (one
 // word at most), so its time is how fast this part can deliver the scorer's
-// input from HBM: the bound the index scorer is compared with. It computes
-// nothing of the method.
+// input from HBM: the bound the index scorer is compared with. Its loads take
+// the scorer's non-temporal cache policy (4 sequences x 2048 pages: 12.0 us
+// against 13.9 us with cached loads). It computes nothing of the method.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(kReadThreads) void k_read_pages(const uint8_t *__re
     for (int u = 0; u < kReadUnroll; ++u) {          // a lane with nothing to read loads the pool's first chunk
       const uint32_t c = c0 + (uint32_t)(u * kReadThreads);
       const size_t off = pg[u] >= 0 ? (size_t)pg[u] * PAGE_BYTES + (size_t)(c % per_page) * 16u : 0;
-      v[u] = *reinterpret_cast<const u32x4 *>(pages + off);
+      v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(pages + off));
       if (pg[u] < 0) v[u] = u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
