@@ -24,6 +24,11 @@ static void launch_mt(const CacheView &c, const uint16_t *q_idx, const float *w,
       launch_shape<FMT, MT, Shape<4, 2, 2>>(c, q_idx, w, B, q, H_I, scores, st, s);
     else
       launch_shape<FMT, MT, Shape<2, 1, 2>>(c, q_idx, w, B, q, H_I, scores, st, s);
+  } else if (pages >= 512 * 32) {         // >= 512 workgroups of 32 pages: two per CU with the longer ones
+    // (32 ragged sequences, 8K-256K: step 105.5 against 107.4 us for 4 x 4 x 2,
+    // scorer 70.1 against 72.6; 4 sequences x 2048 pages, 256 workgroups of 32
+    // pages, ran 32.4 against 29.5 us, so below this size 4 x 4 x 2 stays)
+    launch_shape<FMT, MT, Shape<4, 8, 2>>(c, q_idx, w, B, q, H_I, scores, st, s);
   } else if (pages >= 256 * 16) {         // >= 256 workgroups of 16 pages, two per CU (MXFP4; NVFP4 alike)
     launch_shape<FMT, MT, Shape<4, 4, 2>>(c, q_idx, w, B, q, H_I, scores, st, s);
   } else {

@@ -207,6 +207,9 @@ def test_decode_step_long_with_empty_partitions(mx, b):
     # pages 32..35 taken from its last valid page down, so the earlier page's second
     # half is the wave's fourth chunk), and 8252..8259 over the two halves of page 64
     dict(B=4, ctx_rule=("list", (131072, 4228, 4484, 8260)), topk=16),
+    # the same rows in 4 x 8-page waves (a 4096-entry table: 16384 pages in all, the shape
+    # of 32-page workgroups), 4092..4099 across a workgroup boundary (pages 31 | 32)
+    dict(B=4, ctx_rule=("list", (4100, 4228, 4484, 8260)), topk=16, table_stride=4096),
 ])
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
 def test_decode_step_new_rows_straddle_scorer_workgroups(mx, kw, fmt):
