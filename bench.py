@@ -20,7 +20,8 @@ settle), then the W warmup steps run. Each timed step runs on the
 next of R cache replicas, R at least --replicas (6) and enough that R steps
 touch 512 MB, twice the 256 MB Infinity Cache (the 256K workload: 6 x ~88 MB),
 so that every workload's scan streams from HBM, as a model's layers would, not
-from the MALL; the one-replica (warm) number is reported separately.
+from the MALL; the one-replica (warm) number is reported separately (its index
+pages are copied non-temporally too, so it stays close to the streaming one).
 
 Prints one JSON line (rank 0): the metric (query rows/s), the whole step's
 algorithmic HBM bytes and GB/s, the roofline of the dominant kernel (the index
