@@ -98,6 +98,13 @@ def scorer_source_hash() -> str:
     return h.hexdigest()
 
 
+def cache_replicas(step_bytes: int, at_least: int = 6) -> int:
+    """Cache replicas the timed steps rotate over: at least `at_least`, and
+    enough that their steps touch ROTATION_BYTES together (each replica is
+    then out of the caches when its turn comes again)."""
+    return max(1, at_least, -(-ROTATION_BYTES // max(1, int(step_bytes))))
+
+
 def measured_traffic(workload: str):
     """HBM bytes per scorer launch from the committed rocprofv3 counter summary
     (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy's reading), or None
@@ -261,7 +268,7 @@ def main():
     steps[0].run()
     torch.cuda.synchronize()
     ab = algorithmic_bytes(inp, tables[0].cpu().numpy())
-    R = max(1, args.replicas, -(-ROTATION_BYTES // max(1, ab["total"])))
+    R = cache_replicas(ab["total"], args.replicas)
     caches = [c0]
     for _ in range(R - 1):
         pools = {s_: p.clone() for s_, p in pools0.items()}

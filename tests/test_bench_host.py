@@ -48,3 +48,17 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_cache_replicas_exceed_the_infinity_cache():
+    """The timed steps rotate over enough cache replicas that they touch at
+    least 512 MB (twice the 256 MB Infinity Cache), and never fewer than asked."""
+    import bench
+    assert bench.cache_replicas(88_131_472) == 6            # the 256K workload: 6 x 88 MB = 529 MB
+    assert bench.cache_replicas(16_030_160) == 32           # the 16K FP8 workload: 32 x 16 MB
+    assert bench.cache_replicas(76_650_368) == 7            # 6 x 76.7 MB would be 460 MB
+    assert bench.cache_replicas(401_518_848) == 6           # large steps keep the minimum
+    assert bench.cache_replicas(401_518_848, at_least=2) == 2
+    for b in (1, 10**6, 3 * 10**7, 10**9):
+        r = bench.cache_replicas(b)
+        assert r * b >= bench.ROTATION_BYTES and r >= 6
