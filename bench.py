@@ -216,7 +216,8 @@ def main():
     ap.add_argument("--steps", type=int, default=600)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="headline")
-    ap.add_argument("--replicas", type=int, default=6)
+    ap.add_argument("--replicas", type=int, default=6,
+                    help="at least this many cache replicas (more if their steps would touch under 512 MB)")
     ap.add_argument("--scorer-launches", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--settle-ms", type=float, default=200.0,
